@@ -1,0 +1,227 @@
+"""Benchmark: remapped-position RoPE attention on one MI355X.
+
+A step is one bifocal prefill over the 64K workload (B=1, 32 query / 8 KV
+heads, d=128, w0=4096, s=2, bf16): every prefill step of the hot path
+(rotation-index maps, fused RoPE tile loads, QK^T, online softmax, PV, the
+bifocal merge). The same JSON line also carries the 128K bifocal prefill and
+the 128K-cache bifocal decode (batch 1 and 8), each timed the same way.
+
+Prints ONE JSON line. Inputs are seeded synthetic N(0,1) tensors (workloads/),
+resident in HBM before timing starts. Kernel time comes from HIP events on the
+stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (% bf16 MFMA peak) at 64K/128K; decode KV GB/s at 128K"
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def n_pairs(S: int, window_left: int) -> int:
+    """Kept (i, j) pairs of causal attention with i - j <= window_left (-1: none)."""
+    if window_left < 0 or window_left >= S - 1:
+        return S * (S + 1) // 2
+    w = window_left + 1
+    return w * (w + 1) // 2 + (S - w) * w
+
+
+def prefill_flops(w) -> float:
+    left = w.window_left if w.mode != "bifocal" else -1  # every causal pair counts once in bifocal
+    return 4.0 * w.d * w.Hq * w.B * n_pairs(w.S, left)
+
+
+def kernel_source_sha(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "position_remapped_rope_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(tag: str, sha: str):
+    """HBM traffic per launch from committed rocprofv3 PMC runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"{tag}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != sha:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return ms, wall
+
+
+def bench_prefill(name, steps, warmup):
+    import torch
+    import position_remapped_rope_amd as P
+    import workloads as W
+    w = W.get(name)
+    log(f"{name}: generating inputs")
+    inp = W.make_prefill_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, pos = (inp[n].to(dev) for n in ("q", "k", "v", "pos"))
+    o = torch.empty_like(q)
+    kw = dict(rope_base=w.rope_base, remap_scale=w.remap_scale, window_left=w.window_left)
+
+    def step(_):
+        P.prefill(q, k, v, pos, mode="bifocal", out=o, **kw)
+
+    log(f"{name}: timing {steps} launches")
+    ms, wall = time_launches(step, steps, warmup)
+    flops = prefill_flops(w)
+    avg = sum(ms) / len(ms)
+    tflops = flops / (avg * 1e-3) / 1e12
+    return w, inp, dict(ms=ms, avg_ms=avg, wall_s=wall, flops=flops, tflops=tflops,
+                        frac=tflops / PEAK_BF16_TFLOPS)
+
+
+def bench_decode(name, steps, warmup):
+    import torch
+    import position_remapped_rope_amd as P
+    import workloads as W
+    w = W.get(name)
+    log(f"{name}: generating inputs")
+    inp = W.make_decode_inputs(w)
+    dev = torch.device("cuda:0")
+    kv_bytes = inp["k_cache"].numel() * 2 * 2
+    # rotate between cache copies so the timed reads are not served by the 256 MB MALL
+    copies = max(1, math.ceil(1.5e9 / kv_bytes))
+    caches = []
+    for c in range(copies):
+        caches.append((inp["k_cache"].to(dev), inp["v_cache"].to(dev)))
+    q = inp["q"].to(dev)
+    kv_len = inp["kv_len"].to(dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(P.decode_workspace_size(w.B, w.S, w.Hq, w.d), dtype=torch.uint8, device=dev)
+    kw = dict(rope_base=w.rope_base, remap_scale=w.remap_scale, window_left=w.window_left)
+
+    def step(i):
+        kc, vc = caches[i % copies]
+        P.decode(q, kc, vc, kv_len, mode="bifocal", out=o, workspace=ws, **kw)
+
+    log(f"{name}: timing {steps} launches over {copies} cache copies")
+    ms, wall = time_launches(step, steps, warmup)
+    avg = sum(ms) / len(ms)
+    gbs = kv_bytes / (avg * 1e-3) / 1e9
+    return dict(ms=ms, avg_ms=avg, bytes=kv_bytes, gbs=gbs, frac=gbs / PEAK_HBM_GBS, copies=copies)
+
+
+def cpu_baseline(w, inp, n_rows: int):
+    """The fp64 oracle, as it stands, on a bounded sample of query rows of the same workload."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(12345)
+    rows = np.sort(rng.choice(w.S, size=n_rows, replace=False))
+    q, k, v = (inp[n].double().numpy() for n in ("q", "k", "v"))
+    pos = inp["pos"].numpy()
+    t0 = time.perf_counter()
+    O.prefill_ref(q, k, v, pos, "bifocal", rope_base=w.rope_base, remap_scale=w.remap_scale,
+                  window_left=w.window_left, operand_round="bf16", rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * w.Hq * w.B * float(np.sum(rows + 1))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_rows} uniformly drawn query rows x all {w.Hq} heads of {w.name} "
+                      f"({flops:.3e} algorithmic flop in {dt:.1f} s, fp64 NumPy)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=96)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import position_remapped_rope_amd as P
+    P.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    w, inp, pre = bench_prefill("bifocal_64k", args.steps, args.warmup)
+    sha = kernel_source_sha(["prefill_bf16.hip", "common.hpp", "internal.hpp"])
+    traffic = load_traffic("prefill_bf16_bifocal_64k", sha)
+    result = {
+        "metric": METRIC,
+        "value": round(pre["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["avg_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                   "mode": "bifocal", "w0": w.window_left, "s": w.remap_scale, "rope_base": w.rope_base,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre["frac"], 4), "traffic": traffic,
+                     "kernel": "prefill_bf16_kernel<128, BIFOCAL>",
+                     "algorithmic_flop_per_launch": pre["flops"]},
+    }
+    extra = {}
+    if not args.no_extra:
+        w4, _, pre4 = bench_prefill("bifocal_128k", max(3, args.steps // 2), 1)
+        extra["bifocal_128k"] = {"tflops": round(pre4["tflops"], 2), "frac_bf16_peak": round(pre4["frac"], 4),
+                                 "avg_ms": round(pre4["avg_ms"], 3), "flop": pre4["flops"]}
+        for name, st in (("bifocal_decode_128k_b1", 50), ("bifocal_decode_128k_b8", 10)):
+            d = bench_decode(name, st, 3)
+            extra[name] = {"gbs": round(d["gbs"], 1), "frac_hbm_peak": round(d["frac"], 4),
+                           "avg_us": round(d["avg_ms"] * 1e3, 2), "kv_bytes": d["bytes"],
+                           "cache_copies": d["copies"]}
+            torch.cuda.empty_cache()
+    result["extra"] = extra
+    if not args.no_cpu:
+        log("cpu baseline (oracle on sampled rows)")
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * prope.h - C ABI of the remapped-position RoPE attention library (gfx950).
+ *
+ * Causal attention with rotary position embedding applied on the fly under
+ * remapped position ids:
+ *   - NoPE global attention ("Periodic RoPE for Infinite Context LLMs",
+ *     section 3.3, Eq. (6)): scores q.k / sqrt(d), no rotation;
+ *   - RoPE attention on caller ids, optionally periodic (same page, section
+ *     3.1 Eq. (1)-(3) and section 3.2 Eq. (4)-(5): rotate by p mod P) and
+ *     optionally restricted to a causal sliding window; EndPrompt's
+ *     two-segment ids are just an id array in this mode;
+ *   - Jet-Long bifocal attention ("Jet-Long: Efficient Long-Context Extension
+ *     with Dynamic Bifocal RoPE", section 3, Eq. (1)): keys within w0 of the
+ *     query score with RoPE at the true ids, farther keys with RoPE at ids
+ *     floor(p / s) (section 3.1, Eq. (3)); the two parts are merged through
+ *     partial softmax statistics (section 3.3, Eq. (7)); decode applies the
+ *     correction rotation of section 3.2, Eq. (5)-(6) to a cache of
+ *     base-rotated keys.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent),
+ *     contiguous, in the layouts stated below; `params` is a HOST pointer.
+ *   - The caller owns every buffer. The library allocates no device memory,
+ *     keeps no state between calls and may be called from several threads.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *     and return without synchronising. Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated on the host before any HIP call; a bad argument
+ *     returns PROPE_ERR_INVALID_ARG (or PROPE_ERR_UNSUPPORTED for a valid
+ *     but unimplemented combination) and enqueues nothing. A failed launch
+ *     returns PROPE_ERR_HIP.
+ *   - RoPE pairs adjacent coordinates (2i, 2i+1) and uses frequency
+ *     theta_i = rope_base^(-2i/d) for pair i. Angles are formed from an exact
+ *     64-bit fixed-point phase of p * theta_i / (2 pi), so ids up to 2^31 - 1
+ *     keep full float32 angle accuracy.
+ *   - Masks and bifocal routing use token indices (query index i, key index
+ *     j); position ids only drive rotations.
+ */
+#ifndef PROPE_H
+#define PROPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PROPE_VERSION 1
+
+typedef enum {
+  PROPE_OK = 0,
+  PROPE_ERR_INVALID_ARG = -1,
+  PROPE_ERR_UNSUPPORTED = -2,
+  PROPE_ERR_WORKSPACE = -3,
+  PROPE_ERR_HIP = -4
+} prope_status;
+
+typedef enum { PROPE_BF16 = 0, PROPE_FP32 = 1 } prope_dtype;
+
+typedef enum {
+  PROPE_NOPE = 0,    /* no rotation (P-RoPE page, Eq. (6))                          */
+  PROPE_ROPE = 1,    /* rotate by ids, mod `period` if period > 0 (Eq. (4)-(5))     */
+  PROPE_BIFOCAL = 2  /* Jet-Long Eq. (1): local iff i - j <= window_left, else the
+                        remote view at ids floor(p / remap_scale)                   */
+} prope_mode;
+
+typedef struct {
+  int32_t mode;          /* prope_mode                                                   */
+  int32_t period;        /* P >= 0; 0 = no period. ROPE mode only (else must be 0)       */
+  int32_t remap_scale;   /* s >= 1, the integer group size G of Jet-Long Eq. (2)-(3).
+                            BIFOCAL only (must be 1 otherwise)                           */
+  int32_t window_left;   /* NOPE/ROPE: keys with i - j > window_left are masked; -1 = no
+                            window (full causal). The P-RoPE window of W keys is W - 1.
+                            BIFOCAL: w0 >= -1, routing only; -1 = every key remote        */
+  double rope_base;      /* Theta > 1 (e.g. 1e4, 1e6); ignored by NOPE                    */
+  float softmax_scale;   /* > 0, or 0 for 1/sqrt(d)                                      */
+  int32_t reserved;      /* must be 0                                                    */
+} prope_params;
+
+/*
+ * Prefill: O = softmax(mask(scores)) V for every query row, all heads.
+ *   q [B,S,Hq,d], k [B,S,Hkv,d], v [B,S,Hkv,d], o [B,S,Hq,d]: dtype `dt`,
+ *     q and k UNROTATED (rotation is fused into the kernel's tile loads).
+ *   lse [B,Hq,S] float32, natural-log log-sum-exp of each row's kept scaled
+ *     scores; may be NULL.
+ *   pos [B,S] int32 position ids, each >= 0 (NOPE: ignored, may be NULL).
+ *   Query head h reads KV head h / (Hq / Hkv); Hq % Hkv must be 0.
+ *   d in {64, 128}; 1 <= S; 1 <= B; bf16 or fp32.
+ *   Rows with no kept key (impossible: the key j = i is always kept) would
+ *   get O = 0 and lse = -inf.
+ */
+int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int dt,
+                       const prope_params* params, void* stream);
+
+/*
+ * Decode: one new query token per sequence against a KV cache.
+ *   q [B,Hq,d]: the new token's query ALREADY rotated at its own position
+ *     kv_len[b]-1 (the base view, Jet-Long Eq. (6)'s q_local).
+ *   k_cache, v_cache [B,Lmax,Hkv,d]: keys rotated at their own index (Jet-Long
+ *     Eq. (4)); the cache is never modified.
+ *   kv_len [B] int32 device array, 1 <= kv_len[b] <= Lmax, counting the new
+ *     token (its key is at index kv_len[b]-1).
+ *   o [B,Hq,d] dtype `dt`; lse [B,Hq] float32, may be NULL.
+ *   BIFOCAL: keys with (kv_len-1) - j <= w0 score q.k; farther keys score
+ *     RoPE(q, dq).RoPE(k_j, dk_j) with dq = floor(p_q/s) - p_q and
+ *     dk_j = floor(j/s) - j (Jet-Long Eq. (5)-(6)), computed in registers.
+ *   NOPE/ROPE: scores q.k_j (q and cache already carry the layer's rotation),
+ *     keys beyond window_left masked. `period` must be 0.
+ *   workspace: caller-owned device buffer of at least
+ *     prope_decode_workspace_size(B, Lmax, Hq, d) bytes (split-K partials);
+ *     too small -> PROPE_ERR_WORKSPACE. bf16 only.
+ */
+size_t prope_decode_workspace_size(int B, int Lmax, int Hq, int d);
+int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int32_t* kv_len, int B, int Lmax, int Hq, int Hkv, int d, int dt,
+                      const prope_params* params, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * y = R_pos x per token and head (P-RoPE page, Eq. (2)): x, y [B,S,H,d] of
+ * dtype `dt`, pos [B,S] int32 (any sign: a negative id rotates backwards, which
+ * applies Jet-Long's Eq. (6) corrections). y may alias x exactly. d even,
+ * 2 <= d <= 256. Builds the base-rotated cache of Jet-Long Eq. (4).
+ */
+int prope_rope_apply(const void* x, void* y, const int32_t* pos, int B, int S, int H, int d,
+                     int dt, double rope_base, void* stream);
+
+/* Jet-Long Eq. (2): G = max(1, ceil(L / w_pretrained)); returns -1 on bad input. */
+int prope_group_size(int64_t L, int64_t w_pretrained);
+
+/* Static string for a status code (never NULL). */
+const char* prope_status_string(int status);
+
+int prope_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PROPE_H */

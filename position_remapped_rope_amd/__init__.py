@@ -1,0 +1,193 @@
+"""Python binding of libprope (remapped-position RoPE attention on gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library behind the C ABI declared in include/prope.h. PyTorch supplies device
+memory and the current stream. If the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["NOPE", "ROPE", "BIFOCAL", "PropeError", "lib", "lib_path", "rope_apply", "prefill",
+           "decode", "decode_workspace_size", "group_size", "status_string", "EXPORTED_SYMBOLS"]
+
+NOPE, ROPE, BIFOCAL = 0, 1, 2
+_MODES = {"nope": NOPE, "rope": ROPE, "bifocal": BIFOCAL}
+BF16, FP32 = 0, 1
+
+EXPORTED_SYMBOLS = ("prope_attn_prefill", "prope_attn_decode", "prope_decode_workspace_size",
+                    "prope_rope_apply", "prope_group_size", "prope_status_string", "prope_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libprope.so")
+
+
+class PropeError(RuntimeError):
+    pass
+
+
+class PropeParams(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("period", ctypes.c_int32),
+                ("remap_scale", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libprope.so (once). Raises PropeError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise PropeError(f"{path} is missing: build it with `python -m position_remapped_rope_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.prope_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     ctypes.POINTER(PropeParams), vp]
+    L.prope_attn_prefill.restype = i32
+    L.prope_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                    ctypes.POINTER(PropeParams), vp, ctypes.c_size_t, vp]
+    L.prope_attn_decode.restype = i32
+    L.prope_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.prope_decode_workspace_size.restype = ctypes.c_size_t
+    L.prope_rope_apply.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_double, vp]
+    L.prope_rope_apply.restype = i32
+    L.prope_group_size.argtypes = [i64, i64]
+    L.prope_group_size.restype = i32
+    L.prope_status_string.argtypes = [i32]
+    L.prope_status_string.restype = ctypes.c_char_p
+    L.prope_version.argtypes = []
+    L.prope_version.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return lib().prope_status_string(code).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        raise PropeError(status_string(code))
+
+
+def _params(mode, rope_base, period, remap_scale, window_left, softmax_scale) -> PropeParams:
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    return PropeParams(m, int(period), int(remap_scale), int(window_left), float(rope_base),
+                       float(softmax_scale), 0)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise PropeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise PropeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise PropeError(f"{name} must be contiguous")
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def group_size(L: int, w_pretrained: int) -> int:
+    return lib().prope_group_size(int(L), int(w_pretrained))
+
+
+def decode_workspace_size(B: int, Lmax: int, Hq: int, d: int) -> int:
+    return lib().prope_decode_workspace_size(B, Lmax, Hq, d)
+
+
+def rope_apply(x, pos, rope_base: float, out=None):
+    """y = R_pos x for x [B,S,H,d] (bf16/fp32) and pos int32 [B,S]; out may be x."""
+    import torch
+    L = lib()
+    _dev(x, "x"); _dev(pos, "pos")
+    if pos.dtype != torch.int32 or x.dim() != 4 or tuple(pos.shape) != tuple(x.shape[:2]):
+        raise PropeError("x must be [B,S,H,d] and pos int32 [B,S]")
+    y = torch.empty_like(x) if out is None else out
+    _dev(y, "out")
+    B, S, H, d = x.shape
+    _check(L.prope_rope_apply(_ptr(x), _ptr(y), _ptr(pos), B, S, H, d, _dtype_code(x),
+                              float(rope_base), _stream(x)))
+    return y
+
+
+def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
+            remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
+            out=None, lse=None, return_lse: bool = False):
+    """Causal attention with RoPE fused under remapped ids (see include/prope.h).
+
+    q [B,S,Hq,d], k/v [B,S,Hkv,d] unrotated; pos int32 [B,S] (None for NoPE).
+    Returns O [B,S,Hq,d] (and LSE float32 [B,Hq,S] if return_lse).
+    """
+    import torch
+    L = lib()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (pos, "pos"), (out, "out"), (lse, "lse")):
+        _dev(t, n)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise PropeError("k and v must be [B,S,Hkv,d] with q's dtype")
+    if pos is not None and (pos.dtype != torch.int32 or tuple(pos.shape) != (B, S)):
+        raise PropeError("pos must be int32 [B,S]")
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale)
+    _check(L.prope_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos),
+                                B, S, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
+           remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
+           out=None, lse=None, workspace=None, return_lse: bool = False):
+    """One decode step: q [B,Hq,d] base-rotated, caches [B,Lmax,Hkv,d], kv_len int32 [B]."""
+    import torch
+    L = lib()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_len, "kv_len"),
+                 (out, "out"), (lse, "lse"), (workspace, "workspace")):
+        _dev(t, n)
+    B, Hq, d = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, Lmax, Hkv, d) or v_cache.shape != k_cache.shape:
+        raise PropeError("caches must be [B,Lmax,Hkv,d]")
+    if kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,):
+        raise PropeError("kv_len must be int32 [B]")
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = L.prope_decode_workspace_size(B, Lmax, Hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    p = _params(mode, rope_base, 0, remap_scale, window_left, softmax_scale)
+    _check(L.prope_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
+                               _ptr(kv_len), B, Lmax, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(q)))
+    return (o, lse) if return_lse else o

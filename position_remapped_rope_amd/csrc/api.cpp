@@ -1,0 +1,174 @@
+// C ABI of the library: argument validation, launch configuration, dispatch.
+// Every check runs on the host before any HIP call, so a rejected call has no
+// side effect on the device or the stream.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/prope.h"
+#include "internal.hpp"
+
+namespace prope {
+
+void fill_rope_freq(RopeFreq& f, int d, double base) {
+  // F_i = round(theta_i / (2 pi) * 2^64), theta_i = base^(-2i/d) (P-RoPE page, Eq. (1)).
+  const long double two_pi = 2.0L * acosl(-1.0L);
+  for (int i = 0; i < kMaxPairs; ++i) {
+    uint64_t F = 0;
+    if (i < d / 2) {
+      const long double theta = powl(static_cast<long double>(base), -2.0L * i / d);
+      const long double turns = theta / two_pi * 18446744073709551616.0L;  // * 2^64
+      F = static_cast<uint64_t>(turns + 0.5L);
+    }
+    f.lo[i] = static_cast<uint32_t>(F);
+    f.hi[i] = static_cast<uint32_t>(F >> 32);
+  }
+}
+
+}  // namespace prope
+
+using namespace prope;
+
+namespace {
+
+bool valid_base(double b) { return isfinite(b) && b > 1.0; }
+
+// Common checks of the mode parameters. `decode` forbids a period (the
+// cache already carries the layer's rotation).
+int check_params(const prope_params* p, bool decode) {
+  if (!p) return PROPE_ERR_INVALID_ARG;
+  if (p->reserved != 0) return PROPE_ERR_INVALID_ARG;
+  if (p->mode != PROPE_NOPE && p->mode != PROPE_ROPE && p->mode != PROPE_BIFOCAL)
+    return PROPE_ERR_INVALID_ARG;
+  if (p->period < 0 || p->remap_scale < 1 || p->window_left < -1) return PROPE_ERR_INVALID_ARG;
+  if (!(p->softmax_scale >= 0.0f) || !isfinite(p->softmax_scale)) return PROPE_ERR_INVALID_ARG;
+  if (p->period != 0 && (p->mode != PROPE_ROPE || decode)) return PROPE_ERR_INVALID_ARG;
+  if (p->remap_scale != 1 && p->mode != PROPE_BIFOCAL) return PROPE_ERR_INVALID_ARG;
+  if (p->mode != PROPE_NOPE && !valid_base(p->rope_base)) return PROPE_ERR_INVALID_ARG;
+  return PROPE_OK;
+}
+
+float scale_log2(const prope_params* p, int d) {
+  const double s = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0 / sqrt(static_cast<double>(d));
+  return static_cast<float>(s * 1.4426950408889634);  // * log2(e)
+}
+
+}  // namespace
+
+extern "C" {
+
+int prope_version(void) { return PROPE_VERSION; }
+
+const char* prope_status_string(int status) {
+  switch (status) {
+    case PROPE_OK: return "PROPE_OK";
+    case PROPE_ERR_INVALID_ARG: return "PROPE_ERR_INVALID_ARG: invalid argument";
+    case PROPE_ERR_UNSUPPORTED: return "PROPE_ERR_UNSUPPORTED: valid but unsupported combination";
+    case PROPE_ERR_WORKSPACE: return "PROPE_ERR_WORKSPACE: workspace too small";
+    case PROPE_ERR_HIP: return "PROPE_ERR_HIP: HIP launch failed";
+    default: return "unknown prope status";
+  }
+}
+
+int prope_group_size(int64_t L, int64_t w_pretrained) {
+  // Jet-Long section 3.1, Eq. (2).
+  if (L < 0 || w_pretrained < 1) return -1;
+  const int64_t g = (L + w_pretrained - 1) / w_pretrained;
+  if (g > INT32_MAX) return -1;
+  return g < 1 ? 1 : static_cast<int>(g);
+}
+
+int prope_rope_apply(const void* x, void* y, const int32_t* pos, int B, int S, int H, int d,
+                     int dt, double rope_base, void* stream) {
+  if (!x || !y || !pos) return PROPE_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || H < 1 || d < 2 || d > 2 * kMaxPairs || (d % 2)) return PROPE_ERR_INVALID_ARG;
+  if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
+  if (!valid_base(rope_base)) return PROPE_ERR_INVALID_ARG;
+  const size_t esz = dt == PROPE_BF16 ? 2 : 4;
+  // exact aliasing is fine; partial overlap is not
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
+  const size_t bytes = size_t(B) * S * H * d * esz;
+  if (xa != ya && xa < ya + bytes && ya < xa + bytes) return PROPE_ERR_INVALID_ARG;
+  if ((d % 8) == 0 ? (xa % 16 || ya % 16) : (xa % (2 * esz) || ya % (2 * esz)))
+    return PROPE_ERR_INVALID_ARG;
+  RopeFreq f;
+  fill_rope_freq(f, d, rope_base);
+  const hipError_t e = launch_rope_apply(x, y, pos, B, S, H, d, dt, f, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PROPE_OK : PROPE_ERR_HIP;
+}
+
+int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int dt,
+                       const prope_params* params, void* stream) {
+  const int pc = check_params(params, false);
+  if (pc != PROPE_OK) return pc;
+  if (!q || !k || !v || !o) return PROPE_ERR_INVALID_ARG;
+  if (!pos && params->mode != PROPE_NOPE) return PROPE_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || (Hq % Hkv)) return PROPE_ERR_INVALID_ARG;
+  if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return PROPE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) % 16)
+    return PROPE_ERR_INVALID_ARG;
+  if (int64_t(B) * S * Hq * d >= (int64_t(1) << 40)) return PROPE_ERR_UNSUPPORTED;
+
+  PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.pos = pos;
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = d;
+  a.G = Hq / Hkv;
+  a.HG = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
+  a.BMp = 256 / a.HG;
+  a.n_pblocks = (S + a.BMp - 1) / a.BMp;
+  a.n_hsub = a.G / a.HG;
+  a.mode = params->mode;
+  a.period = params->period;
+  a.window_left = params->window_left;
+  a.period_div = make_fastdiv(params->period > 0 ? static_cast<uint32_t>(params->period) : 1u);
+  a.scale_div = make_fastdiv(static_cast<uint32_t>(params->remap_scale));
+  a.scale_log2 = scale_log2(params, d);
+  fill_rope_freq(a.f, d, params->mode == PROPE_NOPE ? 10000.0 : params->rope_base);
+  const hipError_t e = dt == PROPE_BF16 ? launch_prefill_bf16(a, static_cast<hipStream_t>(stream))
+                                        : launch_prefill_fp32(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PROPE_OK : PROPE_ERR_HIP;
+}
+
+size_t prope_decode_workspace_size(int B, int Lmax, int Hq, int d) {
+  if (B < 1 || Lmax < 1 || Hq < 1 || d < 1) return 0;
+  const size_t n_chunks = (size_t(Lmax) + kDecodeChunk - 1) / kDecodeChunk;
+  return size_t(B) * Hq * n_chunks * (size_t(d) + 2) * sizeof(float);
+}
+
+int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int32_t* kv_len, int B, int Lmax, int Hq, int Hkv, int d, int dt,
+                      const prope_params* params, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  const int pc = check_params(params, true);
+  if (pc != PROPE_OK) return pc;
+  if (!q || !k_cache || !v_cache || !o || !kv_len || !workspace) return PROPE_ERR_INVALID_ARG;
+  if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || (Hq % Hkv)) return PROPE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return PROPE_ERR_INVALID_ARG;
+  if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
+  if (dt != PROPE_BF16) return PROPE_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 8) return PROPE_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(o) |
+       reinterpret_cast<uintptr_t>(workspace)) % 16)
+    return PROPE_ERR_INVALID_ARG;
+  if (workspace_bytes < prope_decode_workspace_size(B, Lmax, Hq, d)) return PROPE_ERR_WORKSPACE;
+  if (int64_t(B) * Lmax * Hkv * d >= (int64_t(1) << 40)) return PROPE_ERR_UNSUPPORTED;
+
+  DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_len = kv_len;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv; a.D = d; a.G = Hq / Hkv;
+  a.n_chunks = (Lmax + kDecodeChunk - 1) / kDecodeChunk;
+  a.mode = params->mode;
+  a.window_left = params->window_left;
+  a.scale_div = make_fastdiv(static_cast<uint32_t>(params->remap_scale));
+  a.scale_log2 = scale_log2(params, d);
+  fill_rope_freq(a.f, d, params->mode == PROPE_NOPE ? 10000.0 : params->rope_base);
+  const hipError_t e = launch_decode_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PROPE_OK : PROPE_ERR_HIP;
+}
+
+}  // extern "C"

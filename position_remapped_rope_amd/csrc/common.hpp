@@ -1,0 +1,113 @@
+// Shared device helpers for the remapped-position RoPE kernels (gfx950).
+//
+// RoPE angle (P-RoPE page, section 3.1, Eq. (1)-(2)): pair i of a vector at
+// rotation index r turns by r * theta_i, theta_i = base^(-2i/d). A float32
+// product r * theta_i loses ~1e-2 rad at r ~ 1.3e5, so the angle is formed
+// from an exact fixed-point phase instead: F_i = round(theta_i / (2 pi) * 2^64)
+// (host, long double), and the turn count r * F_i mod 2^64 is computed with
+// integer multiplies; its top 32 bits give the angle in turns in [-1/2, 1/2),
+// which the hardware sine/cosine (argument in revolutions) consume directly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prope {
+
+constexpr int kMaxPairs = 128;  // rope_apply supports d <= 256; attention d <= 128
+
+// Per-pair phase increments, 64-bit fixed-point turns per unit of id, split in
+// 32-bit halves. Passed by value as a kernel argument (1 KiB).
+struct RopeFreq {
+  uint32_t lo[kMaxPairs];
+  uint32_t hi[kMaxPairs];
+};
+
+// Top 32 bits of (r * F) mod 2^64 as a signed fraction of a turn.
+// Works for negative r (two's complement sign extension of r to 64 bits).
+__device__ __forceinline__ float phase_turns(int32_t r, uint32_t flo, uint32_t fhi) {
+  const uint32_t ru = static_cast<uint32_t>(r);
+  uint32_t top = __umulhi(ru, flo) + ru * fhi;
+  if (r < 0) top -= flo;
+  return static_cast<float>(static_cast<int32_t>(top)) * 0x1p-32f;
+}
+
+// sin and cos of 2*pi*t for t in [-1/2, 1/2) (v_sin_f32 / v_cos_f32 take revolutions).
+__device__ __forceinline__ void sincos_turns(float t, float& s, float& c) {
+  s = __builtin_amdgcn_sinf(t);
+  c = __builtin_amdgcn_cosf(t);
+}
+
+__device__ __forceinline__ void rope_sincos(int32_t r, uint32_t flo, uint32_t fhi, float& s,
+                                            float& c) {
+  sincos_turns(phase_turns(r, flo, fhi), s, c);
+}
+
+// ---- bf16 bit helpers ---------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (a in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v.x = static_cast<__bf16>(a);
+  v.y = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float a) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
+}
+
+// Rotate one packed bf16 pair word (x_{2i} low, x_{2i+1} high) by (c, s); returns floats.
+__device__ __forceinline__ void rot_pair(float x0, float x1, float c, float s, float& y0,
+                                         float& y1) {
+  y0 = c * x0 - s * x1;
+  y1 = s * x0 + c * x1;
+}
+
+// ---- division by an invariant integer ---------------------------------
+// Round-up multiply-shift division (Granlund and Montgomery, "Division by
+// Invariant Integers using Multiplication", PLDI 1994): for 1 <= d < 2^31 and
+// 0 <= n < 2^31, n / d == (umulhi(n, magic) + n) >> shift.
+struct FastDiv {
+  uint32_t magic;
+  uint32_t shift;
+  uint32_t div;
+};
+
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.div = d;
+  f.shift = 0;
+  while ((1u << f.shift) < d) ++f.shift;
+  f.magic = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << f.shift) - d)) / d + 1);
+  return f;
+}
+
+__host__ __device__ inline uint32_t umulhi32(uint32_t a, uint32_t b) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(a) * b) >> 32);
+}
+
+__host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+  return (umulhi32(n, f.magic) + n) >> f.shift;
+}
+
+__host__ __device__ inline uint32_t fastmod(uint32_t n, const FastDiv& f) {
+  return n - fastdiv(n, f) * f.div;
+}
+
+// ---- XCD-aware work order ---------------------------------------------
+// Workgroups are handed to the 8 XCDs round-robin (block b -> XCD b % 8).
+// Remap so that each XCD walks one contiguous range of work items: items that
+// share K/V (same batch and KV head) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  constexpr int kXcd = 8;
+  const int q = total / kXcd, r = total % kXcd;
+  const int xcd = bid % kXcd, slot = bid / kXcd;
+  const int start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+  return start + slot;
+}
+
+}  // namespace prope

@@ -1,0 +1,64 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace prope {
+
+enum Mode : int { kNope = 0, kRope = 1, kBifocal = 2 };
+
+// Everything a prefill launch needs; built and validated by the ABI layer.
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* pos;
+  int B, S, Hq, Hkv, D;
+  int G;          // Hq / Hkv
+  int HG;         // query heads of one KV group handled by one workgroup
+  int BMp;        // query positions per workgroup (BMp * HG == rows per workgroup)
+  int n_pblocks;  // ceil(S / BMp)
+  int n_hsub;     // G / HG
+  int mode;
+  int period;       // ROPE: P (0 = none)
+  int window_left;  // NOPE/ROPE: max kept i-j (-1 none); BIFOCAL: w0
+  FastDiv period_div;
+  FastDiv scale_div;
+  float scale_log2;  // softmax scale * log2(e)
+  RopeFreq f;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* kv_len;
+  float* ws;  // [B][Hq][n_chunks][D + 2]
+  int B, Lmax, Hq, Hkv, D, G;
+  int n_chunks;
+  int mode;
+  int window_left;
+  FastDiv scale_div;
+  float scale_log2;
+  RopeFreq f;
+};
+
+constexpr int kDecodeChunk = 512;  // keys per split-K chunk
+
+// Fill F_i = round(theta_i / (2 pi) * 2^64), theta_i = base^(-2i/d), in long double.
+void fill_rope_freq(RopeFreq& f, int d, double base);
+
+hipError_t launch_rope_apply(const void* x, void* y, const int32_t* pos, int B, int S, int H,
+                             int d, int dt, const RopeFreq& f, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_fp32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace prope

@@ -1,0 +1,95 @@
+"""Helpers shared by the GPU parity tests: run the HIP library through its
+binding, run the oracle on the same seeded inputs, compare."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle as O
+import position_remapped_rope_amd as P
+import workloads as W
+
+# bf16 gate stated for the method: max-abs 2e-2 and mean-relative (L1 ratio) 5e-3;
+# fp32 gate: max-abs 1e-4.
+TOL = {"bf16": dict(max_abs=2e-2, mean_rel=5e-3), "fp32": dict(max_abs=1e-4, mean_rel=1e-5)}
+# LSE: scores are exact products of the same (rounded) operands, accumulated in fp32
+LSE_TOL = {"bf16": 2e-3, "fp32": 1e-5}
+
+
+def log(msg: str):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    diff = np.abs(got - ref)
+    return float(diff.max()), float(diff.sum() / max(np.abs(ref).sum(), 1e-300))
+
+
+def assert_close(got, ref, dtype, what=""):
+    mx, mr = errors(np.asarray(got, np.float64), np.asarray(ref, np.float64))
+    tol = TOL[dtype]
+    log(f"{what}: max_abs={mx:.3e} mean_rel={mr:.3e}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert mx <= tol["max_abs"] and mr <= tol["mean_rel"], f"{what}: max_abs={mx} mean_rel={mr}"
+    return mx, mr
+
+
+def to_np(t) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def gpu_prefill(inputs, mode, **kw):
+    dev = torch.device("cuda:0")
+    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    pos = inputs["pos"].to(dev)
+    o, lse = P.prefill(q, k, v, pos if mode != "nope" else None, mode=mode, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_prefill(inputs, mode, dtype, rows=None, **kw):
+    q, k, v = (to_np(inputs[n]) for n in ("q", "k", "v"))
+    pos = inputs["pos"].numpy()
+    kw = {("softmax_scale" if k_ == "softmax_scale" else k_): v_ for k_, v_ in kw.items()}
+    if kw.get("softmax_scale", 0.0) == 0.0:
+        kw.pop("softmax_scale", None)
+    return O.prefill_ref(q, k, v, pos, mode, operand_round=dtype, rows=rows, **kw)
+
+
+def check_prefill(inputs, mode, dtype, rows=None, what="", **kw):
+    t0 = time.time()
+    o, lse = gpu_prefill(inputs, mode, **kw)
+    t1 = time.time()
+    o_ref, lse_ref = oracle_prefill(inputs, mode, dtype, rows=rows, **kw)
+    t2 = time.time()
+    o_np, lse_np = to_np(o), lse.cpu().numpy()
+    if rows is not None:
+        o_np = o_np[:, rows]
+        lse_np = lse_np[:, :, rows]
+    log(f"{what}: gpu {t1 - t0:.2f}s oracle {t2 - t1:.2f}s")
+    res = assert_close(o_np, o_ref, dtype, what)
+    lerr = float(np.max(np.abs(lse_np - lse_ref)))
+    log(f"{what}: lse max_abs={lerr:.3e}")
+    assert lerr <= LSE_TOL[dtype], f"{what}: lse error {lerr}"
+    return res
+
+
+def gpu_decode(inputs, **kw):
+    dev = torch.device("cuda:0")
+    q, kc, vc = (inputs[n].to(dev) for n in ("q", "k_cache", "v_cache"))
+    kv_len = inputs["kv_len"].to(dev)
+    o, lse = P.decode(q, kc, vc, kv_len, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_decode(inputs, mode, **kw):
+    kw = dict(kw)
+    if kw.get("softmax_scale", 0.0) == 0.0:
+        kw.pop("softmax_scale", None)
+    return O.decode_ref(to_np(inputs["q"]), to_np(inputs["k_cache"]), to_np(inputs["v_cache"]),
+                        inputs["kv_len"].numpy(), mode, **kw)

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import position_remapped_rope_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prope.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(P.lib_path()),
+                                reason="libprope.so not built (python -m position_remapped_rope_amd.build)")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced by rejected calls
+
+
+def _header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(prope_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_symbols_exported():
+    names = _header_functions()
+    assert set(names) == set(P.EXPORTED_SYMBOLS)
+    L = ctypes.CDLL(P.lib_path())
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", P.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (prope_[a-z_]+)\b", out))
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version():
+    L = P.lib()
+    assert L.prope_version() == 1
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, 12345):
+        assert isinstance(P.status_string(code), str) and P.status_string(code)
+
+
+def test_group_size_golden():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "group_size.json")))
+    for L_, G in g["cases"]:
+        assert P.group_size(L_, g["w_pretrained"]) == G
+    assert P.group_size(10, 0) == -1 and P.group_size(-1, 5) == -1
+
+
+def _params(**kw):
+    d = dict(mode=P.BIFOCAL, period=0, remap_scale=2, window_left=8, rope_base=1e6, softmax_scale=0.0, reserved=0)
+    d.update(kw)
+    return P.PropeParams(d["mode"], d["period"], d["remap_scale"], d["window_left"], d["rope_base"],
+                         d["softmax_scale"], d["reserved"])
+
+
+def _prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos=FAKE, B=1, S=16, Hq=4, Hkv=2, d=128, dt=0,
+             params=None, byref=True):
+    L = P.lib()
+    p = _params() if params is None else params
+    return L.prope_attn_prefill(q, k, v, o, lse, pos, B, S, Hq, Hkv, d, dt,
+                                ctypes.byref(p) if byref else None, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(pos=None),
+    dict(B=0), dict(S=0), dict(Hq=0), dict(Hkv=0), dict(Hq=6, Hkv=4),
+    dict(d=96), dict(d=256), dict(d=32), dict(dt=7),
+    dict(q=FAKE + 8),
+    dict(params=_params(remap_scale=0)), dict(params=_params(period=-1)),
+    dict(params=_params(period=8)),                       # period only with ROPE
+    dict(params=_params(mode=P.ROPE, remap_scale=2)),     # remap_scale only with BIFOCAL
+    dict(params=_params(window_left=-2)), dict(params=_params(mode=5)),
+    dict(params=_params(rope_base=1.0)), dict(params=_params(rope_base=float("nan"))),
+    dict(params=_params(softmax_scale=-1.0)), dict(params=_params(reserved=1)),
+    dict(byref=False),
+])
+def test_prefill_rejects(kw):
+    assert _prefill(**kw) == INVALID
+
+
+def test_prefill_nope_allows_null_pos_but_rope_does_not():
+    assert _prefill(pos=None, params=_params(mode=P.ROPE, remap_scale=1)) == INVALID
+
+
+def _decode(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, kv_len=FAKE, B=1, Lmax=4096, Hq=32, Hkv=8, d=128, dt=0,
+            params=None, ws=FAKE, ws_bytes=None):
+    L = P.lib()
+    p = _params() if params is None else params
+    if ws_bytes is None:
+        ws_bytes = L.prope_decode_workspace_size(B, Lmax, Hq, d)
+    return L.prope_attn_decode(q, kc, vc, o, None, kv_len, B, Lmax, Hq, Hkv, d, dt, ctypes.byref(p),
+                               ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(kv_len=None), INVALID), (dict(ws=None), INVALID),
+    (dict(Lmax=0), INVALID), (dict(Hq=30, Hkv=8), INVALID), (dict(d=80), INVALID),
+    (dict(params=_params(mode=P.ROPE, remap_scale=1, period=16)), INVALID),
+    (dict(dt=1), UNSUPPORTED), (dict(Hq=64, Hkv=4), UNSUPPORTED),
+    (dict(ws_bytes=100), WORKSPACE),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_workspace_size_formula():
+    L = P.lib()
+    # [B][Hq][ceil(Lmax / 512)][d + 2] float32 partials
+    assert L.prope_decode_workspace_size(1, 131072, 32, 128) == 1 * 32 * 256 * 130 * 4
+    assert L.prope_decode_workspace_size(8, 1000, 4, 64) == 8 * 4 * 2 * 66 * 4
+    assert L.prope_decode_workspace_size(0, 10, 4, 64) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(pos=None), dict(d=3), dict(d=258), dict(B=0), dict(base=0.5), dict(dt=2),
+    dict(y=FAKE + 64),  # partial overlap with x
+])
+def test_rope_apply_rejects(kw):
+    L = P.lib()
+    a = dict(x=FAKE, y=FAKE + (1 << 24), pos=FAKE, B=1, S=8, H=2, d=64, dt=0, base=1e4)
+    a.update(kw)
+    assert L.prope_rope_apply(a["x"], a["y"], a["pos"], a["B"], a["S"], a["H"], a["d"], a["dt"],
+                              a["base"], None) == INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(P, "_lib", None)
+    monkeypatch.setattr(P, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(P.PropeError):
+        P.lib()

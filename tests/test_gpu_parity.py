@@ -1,0 +1,194 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded inputs. Small shapes span several tiles, ragged tails and the
+degenerate cases; the full-size workloads are checked on all rows (EndPrompt,
+P-RoPE/NoPE, decode) or on stratified sampled rows (64K/128K bifocal)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import position_remapped_rope_amd as P
+import workloads as W
+from parity import (assert_close, check_prefill, gpu_decode, log, oracle_decode, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, S, Hq, Hkv, d, dtype, seed, ids=None):
+    w = W.Workload("t", "prefill", B=B, S=S, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, mode="rope",
+                   rope_base=1e4, seed=seed)
+    inp = W.make_prefill_inputs(w)
+    if ids is not None:
+        inp["pos"] = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(ids, (B, S)).astype(np.int32)))
+    return inp
+
+
+# ------------------------------------------------------------------ rope_apply
+
+@pytest.mark.parametrize("dtype,d,H", [("bf16", 128, 8), ("fp32", 64, 3), ("bf16", 6, 2), ("fp32", 256, 1)])
+def test_rope_apply_matches_oracle(dtype, d, H):
+    rng = np.random.default_rng(d + H)
+    B, S = 2, 300
+    x32 = rng.standard_normal((B, S, H, d)).astype(np.float32)
+    x = W.to_dtype_tensor(x32, dtype)
+    pos = rng.integers(-140000, 140000, size=(B, S)).astype(np.int32)
+    pos[0, :4] = [0, 1, 2**31 - 1, -2**31 + 1]
+    base = 1e6
+    y = P.rope_apply(x.cuda(), torch.from_numpy(pos).cuda(), base)
+    torch.cuda.synchronize()
+    ref = O.rope_apply_ref(to_np(x), pos.astype(np.int64), base)
+    got = to_np(y)
+    if dtype == "bf16":
+        # one rounding of an fp32-accurate result: within one bf16 ulp of the exact value
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        assert np.all(np.abs(got - ref) <= ulp * 1.0 + 1e-6), float(np.max(np.abs(got - ref) / ulp))
+    else:
+        err = float(np.max(np.abs(got - ref)))
+        log(f"rope_apply fp32 d={d}: max_abs={err:.3e}")
+        assert err < 2e-6 * max(1.0, float(np.max(np.abs(ref))))
+
+
+def test_rope_apply_in_place():
+    x = W.to_dtype_tensor(np.random.default_rng(5).standard_normal((1, 64, 4, 128)).astype(np.float32), "bf16").cuda()
+    pos = torch.arange(64, dtype=torch.int32).reshape(1, 64).cuda()
+    y = P.rope_apply(x, pos, 1e4)
+    x2 = x.clone()
+    P.rope_apply(x2, pos, 1e4, out=x2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, x2)
+
+
+# ------------------------------------------------------------------ prefill, small shapes
+
+SMALL = [
+    # name, (B, S, Hq, Hkv, d, dtype), mode, kwargs, ids
+    ("nope_gqa4_ragged", (2, 300, 8, 2, 128, "bf16"), "nope", {}, None),
+    ("nope_mha_d64", (1, 130, 2, 2, 64, "bf16"), "nope", {}, None),
+    ("rope_period_window", (1, 517, 4, 4, 64, "bf16"), "rope", dict(rope_base=1e4, period=128, window_left=100), None),
+    ("rope_self_only", (1, 200, 6, 3, 128, "bf16"), "rope", dict(rope_base=1e4, window_left=0), None),
+    ("rope_gqa3", (1, 190, 6, 2, 128, "bf16"), "rope", dict(rope_base=1e6), None),
+    ("rope_endprompt_ids", (1, 256, 4, 4, 128, "bf16"), "rope", dict(rope_base=1e4), W.endprompt_ids()),
+    ("rope_huge_ids", (1, 160, 4, 2, 128, "bf16"), "rope", dict(rope_base=1e4),
+     (np.arange(160) + (1 << 30)).astype(np.int32)),
+    ("bifocal_gqa8", (1, 700, 8, 1, 128, "bf16"), "bifocal", dict(rope_base=1e6, remap_scale=3, window_left=150), None),
+    ("bifocal_w0_zero", (1, 333, 4, 2, 64, "bf16"), "bifocal", dict(rope_base=1e6, remap_scale=2, window_left=0), None),
+    ("bifocal_all_remote", (1, 260, 4, 1, 128, "bf16"), "bifocal", dict(rope_base=1e6, remap_scale=4, window_left=-1), None),
+    ("bifocal_all_local", (1, 130, 4, 1, 128, "bf16"), "bifocal", dict(rope_base=1e6, remap_scale=4, window_left=500), None),
+    ("bifocal_s1", (2, 257, 4, 2, 128, "bf16"), "bifocal", dict(rope_base=1e6, remap_scale=1, window_left=64), None),
+    ("bifocal_scale_arg", (1, 200, 4, 4, 128, "bf16"), "bifocal",
+     dict(rope_base=1e6, remap_scale=2, window_left=33, softmax_scale=0.05), None),
+    ("one_token", (1, 1, 4, 2, 128, "bf16"), "bifocal", dict(rope_base=1e6, remap_scale=2, window_left=8), None),
+    ("tile_plus_one", (1, 65, 4, 4, 128, "bf16"), "rope", dict(rope_base=1e4, window_left=31), None),
+    ("fp32_nope", (1, 100, 4, 2, 64, "fp32"), "nope", {}, None),
+    ("fp32_bifocal_d128", (1, 150, 4, 2, 128, "fp32"), "bifocal", dict(rope_base=1e6, remap_scale=2, window_left=20), None),
+    ("fp32_rope_period", (2, 90, 2, 1, 64, "fp32"), "rope", dict(rope_base=1e4, period=16, window_left=15), None),
+]
+
+
+@pytest.mark.parametrize("name,shape,mode,kw,ids", SMALL, ids=[c[0] for c in SMALL])
+def test_prefill_small(name, shape, mode, kw, ids):
+    B, S, Hq, Hkv, d, dtype = shape
+    inp = _inputs(B, S, Hq, Hkv, d, dtype, seed=zlib.crc32(name.encode()) % 1000, ids=ids)
+    check_prefill(inp, mode, dtype, what=name, **kw)
+
+
+def test_prefill_period_equals_prereduced_ids():
+    inp = _inputs(1, 300, 4, 4, 128, "bf16", seed=9)
+    o1 = P.prefill(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["pos"].cuda(), mode="rope",
+                   rope_base=1e4, period=64, window_left=63)
+    red = (inp["pos"] % 64).to(torch.int32)
+    o2 = P.prefill(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), red.cuda(), mode="rope",
+                   rope_base=1e4, period=0, window_left=63)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def test_endprompt_fp32_full():
+    w = W.get("endprompt_fp32")
+    inp = W.make_prefill_inputs(w)
+    check_prefill(inp, "rope", "fp32", what=w.name, rope_base=w.rope_base, window_left=-1)
+
+
+@pytest.mark.parametrize("name", ["prope_local_8k", "nope_global_8k"])
+def test_prope_nope_8k_full(name):
+    w = W.get(name)
+    inp = W.make_prefill_inputs(w)
+    kw = dict(window_left=w.window_left)
+    if w.mode == "rope":
+        kw.update(rope_base=w.rope_base, period=w.period)
+    check_prefill(inp, w.mode, "bf16", what=w.name, **kw)
+
+
+@pytest.mark.parametrize("name", ["bifocal_64k", "bifocal_128k"])
+def test_bifocal_full_size_sampled_rows(name):
+    w = W.get(name)
+    log(f"{name}: generating inputs")
+    inp = W.make_prefill_inputs(w)
+    rows = W.stratified_rows(w.S, w.window_left, n_uniform=48, seed=w.seed)
+    log(f"{name}: {len(rows)} sampled rows")
+    check_prefill(inp, "bifocal", "bf16", rows=rows, what=w.name, rope_base=w.rope_base,
+                  remap_scale=w.remap_scale, window_left=w.window_left)
+
+
+# ------------------------------------------------------------------ decode
+
+DEC_SMALL = [
+    ("bifocal_ragged", (3, 2000, 8, 2, 128), "bifocal", dict(rope_base=1e6, remap_scale=4, window_left=300), [2000, 1, 777]),
+    ("bifocal_gqa4_d64", (2, 1500, 8, 2, 64), "bifocal", dict(rope_base=1e4, remap_scale=3, window_left=0), [1500, 513]),
+    ("bifocal_all_remote", (1, 700, 4, 4, 128), "bifocal", dict(rope_base=1e6, remap_scale=2, window_left=-1), [700]),
+    ("nope_window", (2, 1030, 4, 1, 128), "nope", dict(window_left=100), [1030, 40]),
+    ("rope_full", (1, 600, 16, 2, 128), "rope", dict(rope_base=1e4), [600]),
+    ("gqa3", (1, 900, 6, 2, 128), "bifocal", dict(rope_base=1e6, remap_scale=2, window_left=50), [900]),
+]
+
+
+@pytest.mark.parametrize("name,shape,mode,kw,lens", DEC_SMALL, ids=[c[0] for c in DEC_SMALL])
+def test_decode_small(name, shape, mode, kw, lens):
+    B, L, Hq, Hkv, d = shape
+    w = W.Workload("t", "decode", B=B, S=L, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", mode=mode,
+                   rope_base=kw.get("rope_base", 1e4), seed=zlib.crc32(name.encode()) % 1000)
+    inp = W.make_decode_inputs(w)
+    inp["kv_len"] = torch.tensor(lens, dtype=torch.int32)
+    o, lse = gpu_decode(inp, mode=mode, **kw)
+    o_ref, lse_ref = oracle_decode(inp, mode, **kw)
+    assert_close(to_np(o), o_ref, "bf16", name)
+    assert float(np.max(np.abs(lse.cpu().numpy() - lse_ref))) < 2e-3
+
+
+def test_decode_matches_prefill_last_row():
+    """Cache built with rope_apply (Jet-Long Eq. (4)) + decode == last prefill row."""
+    B, S, Hq, Hkv, d = 1, 1100, 8, 2, 128
+    inp = _inputs(B, S, Hq, Hkv, d, "bf16", seed=31)
+    kw = dict(rope_base=1e6, remap_scale=4, window_left=200)
+    q, k, v, pos = (inp[n].cuda() for n in ("q", "k", "v", "pos"))
+    kc = P.rope_apply(k, pos, kw["rope_base"])
+    ql = P.rope_apply(q[:, -1:].contiguous(), pos[:, -1:].contiguous(), kw["rope_base"])[:, 0].contiguous()
+    o_dec = P.decode(ql, kc, v, torch.tensor([S], dtype=torch.int32).cuda(), mode="bifocal", **kw)
+    torch.cuda.synchronize()
+    # the decode oracle on the exact same (rounded) cache and query
+    ref, _ = O.decode_ref(to_np(ql), to_np(kc), to_np(v), [S], "bifocal", **kw)
+    assert_close(to_np(o_dec), ref, "bf16", "decode vs oracle on rope_apply cache")
+    # and the direct prefill oracle's last row (the Eq. (4)-(6) identity), bf16 cache rounding included
+    o_pre, _ = O.prefill_ref(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), inp["pos"].numpy(),
+                             "bifocal", **kw)
+    assert_close(to_np(o_dec), o_pre[:, -1], "bf16", "decode vs prefill oracle last row")
+
+
+@pytest.mark.parametrize("name,check_elems", [("bifocal_decode_128k_b1", [0]), ("bifocal_decode_128k_b8", [0, 5])])
+def test_decode_128k_full(name, check_elems):
+    w = W.get(name)
+    log(f"{name}: generating inputs")
+    inp = W.make_decode_inputs(w)
+    kw = dict(rope_base=w.rope_base, remap_scale=w.remap_scale, window_left=w.window_left)
+    o, lse = gpu_decode(inp, mode="bifocal", **kw)
+    o = to_np(o)
+    for b in check_elems:
+        sub = {"q": inp["q"][b:b + 1], "k_cache": inp["k_cache"][b:b + 1], "v_cache": inp["v_cache"][b:b + 1],
+               "kv_len": inp["kv_len"][b:b + 1]}
+        o_ref, lse_ref = oracle_decode(sub, "bifocal", **kw)
+        assert_close(o[b:b + 1], o_ref, "bf16", f"{name} seq {b}")
+        assert float(np.max(np.abs(lse.cpu().numpy()[b] - lse_ref[0]))) < 2e-3
