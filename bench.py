@@ -171,6 +171,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--only", choices=["prefill_64k", "prefill_128k", "decode_b1", "decode_b8"],
+                    help="time one leg only and print its figures (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -180,6 +182,18 @@ def main():
     import position_remapped_rope_amd as P
     P.lib()  # fail loudly if the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.only:
+        if args.only.startswith("prefill"):
+            name = "bifocal_64k" if args.only == "prefill_64k" else "bifocal_128k"
+            _, _, r = bench_prefill(name, args.steps, args.warmup)
+            r.pop("ms")
+        else:
+            name = "bifocal_decode_128k_b1" if args.only == "decode_b1" else "bifocal_decode_128k_b8"
+            r = bench_decode(name, args.steps, args.warmup)
+            r.pop("ms")
+        print(json.dumps({"only": args.only, "workload": name, **r}), flush=True)
+        return
 
     w, inp, pre = bench_prefill("bifocal_64k", args.steps, args.warmup)
     sha = kernel_source_sha(["prefill_bf16.hip", "common.hpp", "internal.hpp"])

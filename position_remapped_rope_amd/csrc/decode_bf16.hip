@@ -197,27 +197,75 @@ __global__ __launch_bounds__(kDThreads) void decode_split_kernel(const DecodeArg
   }
 }
 
+// One workgroup per (query head, sequence). Threads split the chunk partials
+// (max, sum) and, for O, pairs of (chunk group, 4 dims), then reduce in LDS.
 template <int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a) {
+  constexpr int NT = 256;
+  constexpr int DV = D / 4;       // float4 columns per partial
+  constexpr int CG = NT / DV;     // chunk groups for the O reduction
+  __shared__ float red[NT];
+  __shared__ float4 ored[CG][DV];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
   const int nc = (L + kDecodeChunk - 1) / kDecodeChunk;
-  const size_t head_stride = size_t(a.n_chunks) * (D + 2);
-  const float* wsb = a.ws + (size_t(b) * a.Hq + h) * head_stride;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, wsb[size_t(c) * (D + 2)]);
-  const float Mref = M == -INFINITY ? 0.f : M;
-  float lsum = 0.f;
-  for (int c = 0; c < nc; ++c)
-    lsum = fmaf(__builtin_amdgcn_exp2f(wsb[size_t(c) * (D + 2)] - Mref), wsb[size_t(c) * (D + 2) + 1], lsum);
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float acc = 0.f;
-    for (int c = 0; c < nc; ++c)
-      acc = fmaf(__builtin_amdgcn_exp2f(wsb[size_t(c) * (D + 2)] - Mref), wsb[size_t(c) * (D + 2) + 2 + dd], acc);
-    static_cast<uint16_t*>(a.o)[(size_t(b) * a.Hq + h) * D + dd] = to_bf16(acc * inv);
+  const size_t stride = D + 2;
+  const float* wsb = a.ws + (size_t(b) * a.Hq + h) * size_t(a.n_chunks) * stride;
+
+  float mx = -INFINITY;
+  for (int c = tid; c < nc; c += NT) mx = fmaxf(mx, wsb[size_t(c) * stride]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int off = NT / 2; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
   }
-  if (a.lse && threadIdx.x == 0)
+  const float M = red[0];
+  const float Mref = M == -INFINITY ? 0.f : M;
+  __syncthreads();
+
+  float ls = 0.f;
+  for (int c = tid; c < nc; c += NT)
+    ls = fmaf(__builtin_amdgcn_exp2f(wsb[size_t(c) * stride] - Mref), wsb[size_t(c) * stride + 1], ls);
+  red[tid] = ls;
+  __syncthreads();
+  for (int off = NT / 2; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const float lsum = red[0];
+
+  const int dv = tid % DV, cg = tid / DV;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int c = cg; c < nc; c += CG) {
+    const float* part = wsb + size_t(c) * stride;
+    const float w = __builtin_amdgcn_exp2f(part[0] - Mref);
+    // partial O starts at float offset 2: read as two float2 to stay 8-byte aligned
+    const float2 x0 = *reinterpret_cast<const float2*>(part + 2 + 4 * dv);
+    const float2 x1 = *reinterpret_cast<const float2*>(part + 4 + 4 * dv);
+    acc.x = fmaf(w, x0.x, acc.x);
+    acc.y = fmaf(w, x0.y, acc.y);
+    acc.z = fmaf(w, x1.x, acc.z);
+    acc.w = fmaf(w, x1.y, acc.w);
+  }
+  ored[cg][dv] = acc;
+  __syncthreads();
+  if (tid < DV) {
+    float4 t = ored[0][tid];
+    for (int g = 1; g < CG; ++g) {
+      t.x += ored[g][tid].x;
+      t.y += ored[g][tid].y;
+      t.z += ored[g][tid].z;
+      t.w += ored[g][tid].w;
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint2 packed;
+    packed.x = pack_bf16(t.x * inv, t.y * inv);
+    packed.y = pack_bf16(t.z * inv, t.w * inv);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + (size_t(b) * a.Hq + h) * D + 4 * tid) = packed;
+  }
+  if (a.lse && tid == 0)
     a.lse[size_t(b) * a.Hq + h] = lsum > 0.f ? (M + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
 }
 
@@ -227,7 +275,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.B), dim3(D), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

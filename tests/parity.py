@@ -15,8 +15,12 @@ import workloads as W
 # bf16 gate stated for the method: max-abs 2e-2 and mean-relative (L1 ratio) 5e-3;
 # fp32 gate: max-abs 1e-4.
 TOL = {"bf16": dict(max_abs=2e-2, mean_rel=5e-3), "fp32": dict(max_abs=1e-4, mean_rel=1e-5)}
-# LSE: scores are exact products of the same (rounded) operands, accumulated in fp32
-LSE_TOL = {"bf16": 2e-3, "fp32": 1e-5}
+# LSE is a smooth maximum of a row's scores, so its error is at most the largest
+# score error. A bf16 score can move by one operand ulp times the other operand
+# where the GPU's fp32 rotation and the oracle's fp64 rotation round to different
+# bf16 neighbours: with |q| ~ 3 and keys scaled by 8 that is ~3 * 8 * 2^-8 / sqrt(128)
+# ~ 8e-3 for one flipped coordinate. The gate is 1e-2 (bf16) and 1e-5 (fp32).
+LSE_TOL = {"bf16": 1e-2, "fp32": 1e-5}
 
 
 def log(msg: str):
