@@ -37,7 +37,9 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    # device sources: no kernel relies on NaN semantics, so max() needs no
+    # canonicalisation; host argument checks (api.cpp) keep IEEE NaN handling
+    lang = ["-x", "hip", "-fno-honor-nans"] if src.endswith(".hip") else []
     cmd = [_hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -26,8 +26,11 @@
 // MFMA layout (32x32x16, bf16): S^T = K Q^T, so a lane's output column is a
 // query row: lane l holds row m = l % 32 and keys n = 8*(r/4) + 4*(l/32) + r%4
 // of accumulator register r. The same
-// register order serves directly as the B operand of O^T += V^T P^T, with the
-// A operand V^T read from an LDS copy of V stored transposed.
+// register order serves directly as the B operand of O^T += V^T P^T. V stays
+// row-major in LDS; its transposed A operand comes from ds_read_b64_tr_b16.
+//
+// Overlap. Two waves share each SIMD; while one issues MFMAs the other's
+// vector-ALU work (exponentials, RoPE of the next K tile) can co-issue.
 #include <limits.h>
 
 #include "internal.hpp"
@@ -42,23 +45,42 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 512;  // 8 wavefronts, 2 per SIMD
-constexpr int kVRow = 68;      // transposed-V row stride (elements): 64 keys + pad
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Element (d, n) of the transposed V tile. The row stride of 34 dwords puts
-// consecutive d two banks apart: 8-byte operand reads by 16 lanes (consecutive
-// d) and 4-byte transposing writes by 32 lanes (consecutive key pairs n/2) both
-// hit distinct banks.
-__device__ __forceinline__ int vt_index(int d, int n) { return d * kVRow + n; }
+// Buffer resource over one batch element of a tensor: loads past `bytes`
+// return zero, which pads ragged tiles without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ int bload_i32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 
-struct Pass {
-  int dlo, dhi;  // keep a key iff dlo <= i - j <= dhi
-  int rot;       // 0: none, 1: base ids (mod period if any), 2: remote ids floor(p/s)
-};
+// Workgroup barrier that orders LDS accesses only. Unlike __syncthreads() it
+// does not wait for outstanding global loads, so prefetches stay in flight
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group,
+// lane j names row j/4 and columns 4*(j%4) .. +3 of a 4 x 16 block of 16-bit
+// values; lane i receives column i of the block, rows 0..3 in order.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
 
 template <int MODE>
 __device__ __forceinline__ int rot_index(int p, int rot, const PrefillArgs& a) {
@@ -87,18 +109,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   constexpr int KS = D / 16;            // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;            // 32-row blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int RPP = kThreads / CPR;   // K rows covered by one staging sweep
-  constexpr int NU = kBN / RPP;         // K chunks per thread per tile
-  constexpr int VPW = kThreads / 32;    // V column chunks covered per sweep
-  constexpr int NV = (CPR + VPW - 1) / VPW;  // V chunks (row pairs) per thread per tile
-  constexpr int KRow = D + 8;           // K tile row stride (elements)
-  static_assert(NU >= 1 && NU <= 2 && NV >= 1, "staging layout");
+  constexpr int RPP = kThreads / CPR;   // rows covered by one staging sweep
+  constexpr int NU = kBN / RPP;         // K (and V) chunks per thread per tile
+  constexpr int KRow = D + 8;           // K tile row stride: 16-byte reads of 8 rows hit distinct banks
+  constexpr int VRow = D + 16;          // V tile row stride: transposing reads of 4 rows hit distinct banks
+  static_assert(NU >= 1 && NU <= 2, "staging layout");
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * VRow];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
+  const int group = wave >> 2;  // one wave of each group per SIMD
 
   // ---- work item --------------------------------------------------------
   int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -117,28 +139,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int i1 = min(i0 + 31, S - 1);         // last valid position (i1 < i0: none)
   const int h = kvh * a.G + hsub * a.HG + hl;
 
-  const size_t rowq = size_t(a.Hq) * D, rowk = size_t(a.Hkv) * D;
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + size_t(b) * S * rowq + size_t(h) * D;
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + size_t(b) * S * rowk + size_t(kvh) * D;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + size_t(b) * S * rowk + size_t(kvh) * D;
-  const int32_t* posb = MODE == kNope ? nullptr : a.pos + size_t(b) * S;
+  // byte strides and per-batch buffer resources (loads past the end read 0)
+  const uint32_t rowq_b = uint32_t(a.Hq) * D * 2, rowk_b = uint32_t(a.Hkv) * D * 2;
+  const __amdgpu_buffer_rsrc_t qres = make_rsrc(static_cast<const uint16_t*>(a.q) + size_t(b) * S * a.Hq * D, uint32_t(S) * rowq_b);
+  const __amdgpu_buffer_rsrc_t kres = make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(b) * S * a.Hkv * D, uint32_t(S) * rowk_b);
+  const __amdgpu_buffer_rsrc_t vres = make_rsrc(static_cast<const uint16_t*>(a.v) + size_t(b) * S * a.Hkv * D, uint32_t(S) * rowk_b);
+  const __amdgpu_buffer_rsrc_t pres = make_rsrc(MODE == kNope ? a.q : static_cast<const void*>(a.pos + size_t(b) * S),
+                                                MODE == kNope ? 0u : uint32_t(S) * 4);
 
   // ---- passes and tile ranges ---------------------------------------------
-  Pass pass0, pass1;
-  int npass;
+  // pass 0 (remote keys in BIFOCAL, the only pass otherwise) and pass 1 (the
+  // local window), as plain scalars: keep a key iff dlo <= i - j <= dhi; rot is
+  // 0 (none), 1 (base ids, mod period if any) or 2 (remote ids floor(p/s))
+  int dlo0, dhi0, rot0, dlo1 = 0, dhi1 = -1, rot1 = 0, npass;
   if (MODE == kBifocal) {
     const int w0 = a.window_left;
-    pass0 = {w0 + 1, INT_MAX, 2};
-    pass1 = {0, w0, 1};
+    dlo0 = w0 + 1; dhi0 = INT_MAX; rot0 = 2;
+    dlo1 = 0; dhi1 = w0; rot1 = 1;
     npass = w0 >= 0 ? 2 : 1;
   } else {
-    pass0 = {0, a.window_left < 0 ? INT_MAX : a.window_left, MODE == kNope ? 0 : 1};
-    pass1 = pass0;
+    dlo0 = 0; dhi0 = a.window_left < 0 ? INT_MAX : a.window_left; rot0 = MODE == kNope ? 0 : 1;
     npass = 1;
   }
-  auto tile_range = [&](const Pass& ps, int& tb, int& tc) {
-    const int64_t jlo = max<int64_t>(0, int64_t(P0) - ps.dhi);
-    const int64_t jhi = min<int64_t>(S - 1, int64_t(P1) - ps.dlo);
+  auto tile_range = [&](int dlo, int dhi, int& tb, int& tc) {
+    const int64_t jlo = max<int64_t>(0, int64_t(P0) - dhi);
+    const int64_t jhi = min<int64_t>(S - 1, int64_t(P1) - dlo);
     tb = 0;
     tc = 0;
     if (jhi >= jlo) {
@@ -147,141 +172,137 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     }
   };
   int tb0, tc0, tb1 = 0, tc1 = 0;
-  tile_range(pass0, tb0, tc0);
-  if (npass > 1) tile_range(pass1, tb1, tc1);
+  tile_range(dlo0, dhi0, tb0, tc0);
+  if (npass > 1) tile_range(dlo1, dhi1, tb1, tc1);
   const int T = tc0 + tc1;
-
-  // ---- per-thread staging coordinates --------------------------------------
-  const int sc = tid % CPR;   // 16-byte column chunk of K this thread stages
-  const int sr = tid / CPR;   // first K row this thread stages (second: sr + RPP)
-  const int vp = tid & 31;    // V key pair (rows 2vp, 2vp+1) this thread stages
-  const int vc = tid >> 5;    // first V column chunk this thread stages
-  uint32_t kflo[4], kfhi[4];  // frequencies of the K chunk's 4 pairs
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    kflo[e] = a.f.lo[sc * 4 + e];
-    kfhi[e] = a.f.hi[sc * 4 + e];
-  }
-  // The second K row a thread stages is RPP keys after the first. When the
-  // rotation ids of the two rows differ by the pass's affine step (RPP for base
-  // ids; RPP / s for remote ids when s divides RPP), the second row's cos/sin
-  // are the first row's times the fixed rotation by that step.
-  float estep_c[4], estep_s[4];
-  int id_step = -1;
-
-  u32x4_t kraw[NU], vraw[2 * NV];
-  int kid[NU];
 
   auto tile_of = [&](int t, int& p, int& kt) {
     p = t < tc0 ? 0 : 1;
     kt = p ? tb1 + (t - tc0) : tb0 + t;
   };
 
-  auto set_pass_step = [&](int rot) {
-    id_step = -1;
-    if (MODE == kNope || rot == 0 || NU < 2) return;
-    if (rot == 2) {
-      const uint32_t sdiv = a.scale_div.div;
-      if (RPP % sdiv == 0) id_step = RPP / static_cast<int>(sdiv);
-    } else {
-      id_step = RPP;  // (a period wrap inside the pair of rows is caught by the check below)
-    }
-    if (id_step >= 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rope_sincos(id_step, kflo[e], kfhi[e], estep_s[e], estep_c[e]);
-    }
-  };
+  // ---- per-thread staging coordinates --------------------------------------
+  const int sc = tid % CPR;   // 16-byte column chunk this thread stages (K and V)
+  const int sr = tid / CPR;   // first row this thread stages (second: sr + RPP)
+  const uint32_t kcol_b = uint32_t(kvh) * D * 2 + sc * 16;
 
-  auto stage_load = [&](int t) {
-    int p, kt;
-    tile_of(t, p, kt);
-    const int j0 = kt * kBN;
-    const int rot = p ? pass1.rot : pass0.rot;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int j = j0 + sr + RPP * u;
-      const bool ok = j < S;
-      kraw[u] = ok ? *reinterpret_cast<const u32x4_t*>(kg + size_t(j) * rowk + sc * 8) : u32x4_t{0, 0, 0, 0};
-      kid[u] = (ok && rot) ? posb[j] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int j = j0 + 2 * vp;
-      const int c = vc + VPW * u;
-      if (c >= CPR) continue;  // d = 64: half the threads stage no V
-      vraw[2 * u] = j < S ? *reinterpret_cast<const u32x4_t*>(vg + size_t(j) * rowk + c * 8) : u32x4_t{0, 0, 0, 0};
-      vraw[2 * u + 1] = j + 1 < S ? *reinterpret_cast<const u32x4_t*>(vg + size_t(j + 1) * rowk + c * 8) : u32x4_t{0, 0, 0, 0};
-    }
-  };
+  // Per-chunk constants kept in LDS rather than registers: the 4 pair
+  // frequencies of each 16-byte column chunk, and for each rotation kind the
+  // cos/sin of the affine id step between the two K rows a thread stages. The
+  // second K row a thread stages is RPP keys after the first; when their
+  // rotation ids differ by that step (RPP for base ids, RPP / s for remote ids
+  // when s divides RPP) its cos/sin are the first row's times the step's.
+  __shared__ uint2 kfreq[CPR * 4];
+  __shared__ float2 kstep[2][CPR * 4];
+  const int id_step1 = NU > 1 ? RPP : -1;
+  const int sdiv = static_cast<int>(a.scale_div.div);
+  const int id_step2 = (NU > 1 && RPP % sdiv == 0) ? RPP / sdiv : -1;
+  if (MODE != kNope && tid < CPR * 4) {
+    const uint32_t flo = a.f.lo[tid], fhi = a.f.hi[tid];
+    kfreq[tid] = make_uint2(flo, fhi);
+    float s1 = 0.f, c1 = 1.f, s2 = 0.f, c2 = 1.f;
+    if (id_step1 >= 0) rope_sincos(id_step1, flo, fhi, s1, c1);
+    if (id_step2 >= 0) rope_sincos(id_step2, flo, fhi, s2, c2);
+    kstep[0][tid] = make_float2(c1, s1);
+    kstep[1][tid] = make_float2(c2, s2);
+  }
+  __syncthreads();
 
-  auto stage_store = [&](int t, int buf) {
-    int p, kt;
-    tile_of(t, p, kt);
-    const int rot = p ? pass1.rot : pass0.rot;
-    if (MODE != kNope && rot) {
-      float cs[4], sn[4];
-      const int r0 = rot_index<MODE>(kid[0], rot, a);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rope_sincos(r0, kflo[e], kfhi[e], sn[e], cs[e]);
+  u32x4_t kraw[NU], vraw[NU];
+  int kid[NU];
+
+  // global -> registers: K rows of tile tk and V rows of tile tv (either may be >= T: skipped)
+  auto stage_load = [&](int tk, int tv) __attribute__((always_inline)) {
+    if (tk < T) {
+      int p, kt;
+      tile_of(tk, p, kt);
+      const int rot = p ? rot1 : rot0;
+      const uint32_t j0 = uint32_t(kt) * kBN;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        if (u > 0) {
-          const int ru = rot_index<MODE>(kid[u], rot, a);
-          if (id_step >= 0 && ru - r0 == id_step * u) {
+        const uint32_t j = j0 + sr + RPP * u;
+        kraw[u] = bload16(kres, j * rowk_b + kcol_b);
+        kid[u] = (MODE != kNope && rot) ? bload_i32(pres, j * 4) : 0;
+      }
+    }
+    if (tv < T) {
+      int p, kt;
+      tile_of(tv, p, kt);
+      const uint32_t j0 = uint32_t(kt) * kBN;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {  // (cs + i sn) * (estep_c + i estep_s)
-              const float c2 = cs[e] * estep_c[e] - sn[e] * estep_s[e];
-              const float s2 = sn[e] * estep_c[e] + cs[e] * estep_s[e];
-              cs[e] = c2;
-              sn[e] = s2;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rope_sincos(ru, kflo[e], kfhi[e], sn[e], cs[e]);
-          }
-        }
-        u32x4_t y;
+      for (int u = 0; u < NU; ++u) vraw[u] = bload16(vres, (j0 + sr + RPP * u) * rowk_b + kcol_b);
+    }
+  };
+
+  // registers -> LDS: K of tile tk (rotated for its pass) and V of tile tv
+  auto stage_store = [&](int tk, int tv) __attribute__((always_inline)) {
+    if (tk < T) {
+      int p, kt;
+      tile_of(tk, p, kt);
+      uint16_t* dst = Ks[tk & 1];
+      const int rot = p ? rot1 : rot0;
+      if (MODE != kNope && rot) {
+        const int id_step = rot == 2 ? id_step2 : id_step1;
+        uint32_t kflo[4], kfhi[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float y0, y1;
-          rot_pair(bf16_lo(kraw[u][e]), bf16_hi(kraw[u][e]), cs[e], sn[e], y0, y1);
-          y[e] = pack_bf16(y0, y1);
+          const uint2 f = kfreq[sc * 4 + e];
+          kflo[e] = f.x;
+          kfhi[e] = f.y;
         }
-        *reinterpret_cast<u32x4_t*>(&Ks[buf][(sr + RPP * u) * KRow + sc * 8]) = y;
-      }
-    } else {
+        float cs[4], sn[4];
+        const int r0 = rot_index<MODE>(kid[0], rot, a);
 #pragma unroll
-      for (int u = 0; u < NU; ++u)
-        *reinterpret_cast<u32x4_t*>(&Ks[buf][(sr + RPP * u) * KRow + sc * 8]) = kraw[u];
+        for (int e = 0; e < 4; ++e) rope_sincos(r0, kflo[e], kfhi[e], sn[e], cs[e]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          if (u > 0) {
+            const int ru = rot_index<MODE>(kid[u], rot, a);
+            if (id_step >= 0 && ru - r0 == id_step * u) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {  // (cs + i sn) * (step cos + i step sin)
+                const float2 es = kstep[rot - 1][sc * 4 + e];
+                const float c2 = cs[e] * es.x - sn[e] * es.y;
+                const float s2 = sn[e] * es.x + cs[e] * es.y;
+                cs[e] = c2;
+                sn[e] = s2;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) rope_sincos(ru, kflo[e], kfhi[e], sn[e], cs[e]);
+            }
+          }
+          u32x4_t y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float y0, y1;
+            rot_pair(bf16_lo(kraw[u][e]), bf16_hi(kraw[u][e]), cs[e], sn[e], y0, y1);
+            y[e] = pack_bf16(y0, y1);
+          }
+          *reinterpret_cast<u32x4_t*>(&dst[(sr + RPP * u) * KRow + sc * 8]) = y;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPP * u) * KRow + sc * 8]) = kraw[u];
+      }
     }
+    if (tv < T) {
+      uint16_t* dst = Vs[tv & 1];
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      if (vc + VPW * u >= CPR) continue;
-      const int n = 2 * vp;
-      const u32x4_t r0 = vraw[2 * u], r1 = vraw[2 * u + 1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = (vc + VPW * u) * 8 + 2 * e;
-        // column d (low halves) and d+1 (high halves) of rows n, n+1
-        const uint32_t lo = (r0[e] & 0xffffu) | (r1[e] << 16);
-        const uint32_t hi = (r0[e] >> 16) | (r1[e] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&Vt[buf][vt_index(d, n)]) = lo;
-        *reinterpret_cast<uint32_t*>(&Vt[buf][vt_index(d + 1, n)]) = hi;
-      }
+      for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPP * u) * VRow + sc * 8]) = vraw[u];
     }
   };
 
   // ---- query operand (B of S^T = K Q^T): lane holds row lr, dims ks*16 + lg*8 .. +7
   u32x4_t qreg[KS];
-  auto load_q = [&](int p) {
-    const int rot = p ? pass1.rot : pass0.rot;
-    const int i = i0 + lr;
-    const bool ok = i <= i1;
-    const int r = (ok && MODE != kNope && rot) ? rot_index<MODE>(posb[i], rot, a) : 0;
+  auto load_q = [&](int p) __attribute__((always_inline)) {
+    const int rot = p ? rot1 : rot0;
+    const uint32_t i = uint32_t(i0 + lr);
+    const uint32_t qoff = i * rowq_b + uint32_t(h) * D * 2 + lg * 16;
+    const int r = (MODE != kNope && rot) ? rot_index<MODE>(bload_i32(pres, i * 4), rot, a) : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t x = ok ? *reinterpret_cast<const u32x4_t*>(qg + size_t(i) * rowq + ks * 16 + lg * 8)
-                     : u32x4_t{0, 0, 0, 0};
+      u32x4_t x = bload16(qres, qoff + ks * 32);  // rows past the sequence read 0
       if (MODE != kNope && rot) {
         uint32_t flo[4], fhi[4];
 #pragma unroll
@@ -295,6 +316,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     }
   };
 
+  // ---- per-lane LDS addresses of the PV operand (transposing reads of V) ---
+  // A operand of O^T += V^T P^T for d-block db and 16-key step kk: lane (lr, lg)
+  // needs V[16kk + 4lg + e][32db + lr] for e = 0..3 and V[16kk + 8 + 4lg + e][..].
+  const int j15 = lane & 15;
+  const int vrow0 = 4 * lg + (j15 >> 2);
+  const int vcol0 = 16 * (lr >> 4) + 4 * (j15 & 3);
+
   // ---- running statistics ---------------------------------------------------
   f32x16_t oacc[DB];
 #pragma unroll
@@ -305,35 +333,51 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   float l_run = 0.f;        // this lane's share of the running sum
   const float sl2 = a.scale_log2;
 
-  // ---- main loop ------------------------------------------------------------
-  int cur_pass = 0;
-  set_pass_step(pass0.rot);
-  stage_load(0);
+  // does tile t hold any kept (row, key) pair of this wave?
+  auto wave_live = [&](int t, bool& need_mask, int& dlo, int& dhi, int& j0) __attribute__((always_inline)) {
+    int p, kt;
+    tile_of(t, p, kt);
+    dlo = p ? dlo1 : dlo0;
+    dhi = p ? dhi1 : dhi0;
+    j0 = kt * kBN;
+    const int dmin = i0 - (j0 + kBN - 1), dmax = i1 - j0;
+    need_mask = dmin < dlo || dmax > dhi;
+    return i1 >= i0 && dmax >= dlo && dmin <= dhi;
+  };
+
+  auto xhalf_max = [&](float x) __attribute__((always_inline)) {
+    // max with the lane 32 apart (same query row, other half of the keys)
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+
+  // ---- main loop: one barrier per 64-key tile --------------------------------
+  // Iteration t issues the global loads of tile t+1, computes tile t from LDS
+  // (S^T = K Q^T, online softmax, O^T += V^T P^T), then rotates tile t+1's K
+  // into the other LDS buffer.
+  int cur_pass;
+  {
+    int p0, kt0;
+    tile_of(0, p0, kt0);
+    cur_pass = p0;
+  }
+  stage_load(0, 0);
   stage_store(0, 0);
-  load_q(0);
+  load_q(cur_pass);
   __syncthreads();
 
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
     int p, kt;
     tile_of(t, p, kt);
-    if (p != cur_pass) {  // entering the local pass: re-rotate queries and the K step
+    if (p != cur_pass) {  // first tile of the local pass: re-rotate the queries
       cur_pass = p;
       load_q(p);
-      set_pass_step(pass1.rot);
     }
-    if (t + 1 < T) {
-      int pn, ktn;
-      tile_of(t + 1, pn, ktn);
-      if (pn != cur_pass) set_pass_step(pass1.rot);
-      stage_load(t + 1);
-    }
-    const int j0 = kt * kBN;
-    const int dlo = p ? pass1.dlo : pass0.dlo, dhi = p ? pass1.dhi : pass0.dhi;
-    const int dmin = i0 - (j0 + kBN - 1), dmax = i1 - j0;
-    const bool live = i1 >= i0 && dmax >= dlo && dmin <= dhi;
-    if (live) {
-      const bool need_mask = dmin < dlo || dmax > dhi;
+    if (t + 1 < T) stage_load(t + 1, t + 1);
+    bool need_mask;
+    int dlo, dhi, j0;
+    if (wave_live(t, need_mask, dlo, dhi, j0)) {
       // S^T = K Q^T for the 64 keys (two 32-key blocks nb) and the wave's 32 rows
       f32x16_t sacc[2];
 #pragma unroll
@@ -364,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[nb][r], sacc[nb][r + 1]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = xhalf_max(mx);
       const float mnew = fmaxf(m_run, mx * sl2);
       const bool grow = mnew > m_run;
       const float mref = mnew == -INFINITY ? 0.f : mnew;
@@ -380,8 +424,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
           rs += pv;
         }
       l_run = l_run * alpha + rs;
-      // rescale O only when some row of the wave raised its max
-      if (__any(grow)) {
+      if (__any(grow)) {  // rescale O only when some row of the wave raised its max
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -395,23 +438,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
                              pack_bf16(sacc[nb][r0 + 2], sacc[nb][r0 + 3]),
                              pack_bf16(sacc[nb][r0 + 4], sacc[nb][r0 + 5]),
                              pack_bf16(sacc[nb][r0 + 6], sacc[nb][r0 + 7])};
-        const int n = kk * 16 + 4 * lg;
+        const uint16_t* vrow = &Vs[buf][(kk * 16 + vrow0) * VRow + vcol0];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = db * 32 + lr;
-          const u32x2_t va = *reinterpret_cast<const u32x2_t*>(&Vt[buf][vt_index(d, n)]);
-          const u32x2_t vb = *reinterpret_cast<const u32x2_t*>(&Vt[buf][vt_index(d, n + 8)]);
+          const u32x2_t va = lds_read_tr16(vrow + db * 32);
+          const u32x2_t vb = lds_read_tr16(vrow + 8 * VRow + db * 32);
           const u32x4_t vop = {va[0], va[1], vb[0], vb[1]};
           oacc[db] = mfma32x32x16(vop, pop, oacc[db]);
         }
       }
     }
-    if (t + 1 < T) stage_store(t + 1, buf ^ 1);
+    if (t + 1 < T) stage_store(t + 1, t + 1);
     __syncthreads();
   }
 
   // ---- finalize ---------------------------------------------------------------
-  uint16_t* og = static_cast<uint16_t*>(a.o) + size_t(b) * S * rowq + size_t(h) * D;
+  uint16_t* og = static_cast<uint16_t*>(a.o) + size_t(b) * S * a.Hq * D + size_t(h) * D;
+  const size_t rowq = size_t(a.Hq) * D;
   const float l = l_run + __shfl_xor(l_run, 32);
   const int i = i0 + lr;
   if (i <= i1) {
