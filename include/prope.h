@@ -86,7 +86,9 @@ typedef struct {
  *     scores; may be NULL.
  *   pos [B,S] int32 position ids, each >= 0 (NOPE: ignored, may be NULL).
  *   Query head h reads KV head h / (Hq / Hkv); Hq % Hkv must be 0.
- *   d in {64, 128}; 1 <= S; 1 <= B; bf16 or fp32.
+ *   d in {64, 128}; 1 <= S; 1 <= B; bf16 or fp32. One sequence's q slice
+ *   (S * Hq * d elements) must stay under 2^30 elements (32-bit byte offsets),
+ *   else PROPE_ERR_UNSUPPORTED.
  *   Rows with no kept key (impossible: the key j = i is always kept) would
  *   get O = 0 and lse = -inf.
  */
@@ -110,7 +112,9 @@ int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, flo
  *     keys beyond window_left masked. `period` must be 0.
  *   workspace: caller-owned device buffer of at least
  *     prope_decode_workspace_size(B, Lmax, Hq, d) bytes (split-K partials);
- *     too small -> PROPE_ERR_WORKSPACE. bf16 only.
+ *     too small -> PROPE_ERR_WORKSPACE. bf16 only; Hq / Hkv <= 16 and one
+ *     sequence's cache slice (Lmax * Hkv * d * 2 bytes) under 4 GiB, else
+ *     PROPE_ERR_UNSUPPORTED.
  */
 size_t prope_decode_workspace_size(int B, int Lmax, int Hq, int d);
 int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

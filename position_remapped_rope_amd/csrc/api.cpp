@@ -110,7 +110,8 @@ int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, flo
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) % 16)
     return PROPE_ERR_INVALID_ARG;
-  if (int64_t(B) * S * Hq * d >= (int64_t(1) << 40)) return PROPE_ERR_UNSUPPORTED;
+  // one sequence's q/k/v/o slices are addressed with 32-bit byte offsets
+  if (int64_t(S) * Hq * d * 4 >= (int64_t(1) << 32)) return PROPE_ERR_UNSUPPORTED;
 
   PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.pos = pos;
@@ -149,13 +150,14 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
   if (d != 64 && d != 128) return PROPE_ERR_INVALID_ARG;
   if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
   if (dt != PROPE_BF16) return PROPE_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 8) return PROPE_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return PROPE_ERR_UNSUPPORTED;  // query heads of a group fill one 16-wide MFMA tile
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(o) |
        reinterpret_cast<uintptr_t>(workspace)) % 16)
     return PROPE_ERR_INVALID_ARG;
   if (workspace_bytes < prope_decode_workspace_size(B, Lmax, Hq, d)) return PROPE_ERR_WORKSPACE;
-  if (int64_t(B) * Lmax * Hkv * d >= (int64_t(1) << 40)) return PROPE_ERR_UNSUPPORTED;
+  // one sequence's cache slice is addressed with 32-bit byte offsets
+  if (int64_t(Lmax) * Hkv * d * 2 >= (int64_t(1) << 32)) return PROPE_ERR_UNSUPPORTED;
 
   DecodeArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_len = kv_len;

@@ -10,12 +10,20 @@
 // score q . k_j with an optional window.
 //
 // Kernel 1 (split): one workgroup per (chunk of kDecodeChunk keys, KV head,
-// sequence). 16 lanes cover one key's 128 dims (16 B each, coalesced 256-byte
-// rows); the workgroup keeps 16 keys in flight per step, 4 steps unrolled so
-// each lane has 8 independent 16-byte loads outstanding. Every key is scored
-// against all G query heads of its KV group (G-fold reuse of each loaded byte).
-// Partial softmax statistics (row max m, row sum l, unnormalised O) are
-// merged across lane groups in LDS and written to the workspace.
+// sequence); each of its 4 waves streams a quarter of the chunk in steps of 32
+// keys with no workgroup barrier. Per step and wave:
+//   - K rows are loaded straight into the A-operand layout of
+//     v_mfma_f32_16x16x32_bf16 (lane l: key l%16, dims 8*(l/16) + 32*ks ..+7;
+//     16-byte loads, each key's 256 bytes read by 16 lanes), remote keys are
+//     rotated by dk_j in registers and rounded to bf16;
+//   - S^T = K Q^T on MFMA against the G query heads of the KV group (padded to
+//     16 columns: every loaded byte serves all G heads);
+//   - online softmax per head over the step's 32 keys;
+//   - V rows go through a per-wave LDS tile and come back transposed
+//     (ds_read_b64_tr_b16) as the B operand of O = P V on MFMA; the S^T
+//     accumulator layout is already P's A-operand layout.
+// The 4 waves' partial softmax statistics (row max m, row sum l, unnormalised
+// O) are merged in LDS and written to the workspace.
 // Kernel 2 (combine): per (sequence, query head) the chunk partials are
 // merged with log-sum-exp weights (Jet-Long Eq. (7)'s merge with only
 // disjoint parts) into O and the LSE.
@@ -24,28 +32,64 @@
 namespace prope {
 namespace {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kDThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kDThreads = 256;  // 4 waves
+constexpr int kStep = 32;       // keys per wave step (two 16-key MFMA blocks)
 
-template <int LPK>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int off = LPK / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <int D, int MODE, int GM>
-__global__ __launch_bounds__(kDThreads) void decode_split_kernel(const DecodeArgs a) {
-  constexpr int LPK = D / 8;                 // lanes per key
-  constexpr int GROUPS = kDThreads / LPK;    // keys in flight per step
-  __shared__ float red_m[GROUPS][GM];
-  __shared__ float red_l[GROUPS][GM];
-  __shared__ float red_o[GROUPS][GM][D];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// gfx950 ds_read_b64_tr_b16: within each 16-lane group, lane j names row j/4
+// and columns 4*(j%4) .. +3 of a 4 x 16 block of 16-bit values; lane i
+// receives column i of the block, rows 0..3 in order.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// max / sum across the 4 lanes that hold the same head (l, l^16, l^32, l^48)
+__device__ __forceinline__ float xgroup_max(float x) {
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+}
+__device__ __forceinline__ float xgroup_sum(float x) {
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const DecodeArgs a) {
+  constexpr int KSTEPS = D / 32;             // 16x16x32 k-steps over the head dimension
+  constexpr int DBLK = D / 16;               // 16-dim blocks of O
+  constexpr int VROW = D + 16;               // V tile row stride (elements): transposing reads hit distinct banks
+  constexpr int VCHUNKS = kStep * D / 8;     // 16-byte chunks of one V tile
+  constexpr int VPL = VCHUNKS / 64;          // per lane
+  constexpr int WAVES = kDThreads / 64;
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[WAVES][kStep * VROW];
+  __shared__ float red_m[WAVES][16], red_l[WAVES][16];
+  __shared__ float red_o[WAVES][16][D + 4];
 
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, c = tid % LPK, grp = tid / LPK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kl = lane & 15, kg = lane >> 4;
   const int G = a.G;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);  // a length outside [0, Lmax] never reads past the cache
   const int jbeg = chunk * kDecodeChunk;
@@ -62,131 +106,191 @@ __global__ __launch_bounds__(kDThreads) void decode_split_kernel(const DecodeArg
   const int jend = min(L, jbeg + kDecodeChunk);
   const int pq = L - 1;
   const float sl2 = a.scale_log2;
-
-  // query slice (dims c*8 .. c*8+7) of every head in the group, local and remote views
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(kvh) * G) * D + c * 8;
-  float ql[GM][8], qr[GM][8];
-  uint32_t flo[4], fhi[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    flo[e] = a.f.lo[c * 4 + e];
-    fhi[e] = a.f.hi[c * 4 + e];
-  }
-  const int dq = MODE == kBifocal ? static_cast<int>(fastdiv(static_cast<uint32_t>(pq), a.scale_div)) - pq : 0;
-  float qs[4], qc[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) rope_sincos(dq, flo[e], fhi[e], qs[e], qc[e]);
-#pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    u32x4_t w = {0, 0, 0, 0};
-    if (g < G) w = *reinterpret_cast<const u32x4_t*>(qg + size_t(g) * D);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ql[g][2 * e] = bf16_lo(w[e]);
-      ql[g][2 * e + 1] = bf16_hi(w[e]);
-      rot_pair(ql[g][2 * e], ql[g][2 * e + 1], qc[e], qs[e], qr[g][2 * e], qr[g][2 * e + 1]);
-    }
-  }
-
-  float m_run[GM], l_run[GM], o[GM][8];
-#pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
-  }
-
-  const size_t rowk = size_t(a.Hkv) * D;
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + size_t(b) * a.Lmax * rowk + size_t(kvh) * D + c * 8;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + size_t(b) * a.Lmax * rowk + size_t(kvh) * D + c * 8;
   const int w0 = a.window_left;
 
-  for (int jb = jbeg + grp; jb < jend; jb += GROUPS * kUnroll) {
-    u32x4_t kw[kUnroll], vw[kUnroll];
+  // ---- query operand (B of S^T = K Q^T): lane l holds head kl, dims 8kg + 32ks .. +7
+  // in the local view (as given) and the remote view RoPE(q, dq), both bf16.
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(kvh) * G) * D;
+  u32x4_t qloc[KSTEPS], qrem[KSTEPS];
+  const int dq = MODE == kBifocal ? static_cast<int>(fastdiv(static_cast<uint32_t>(pq), a.scale_div)) - pq : 0;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int j = jb + GROUPS * u;
-      const bool ok = j < jend;
-      kw[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kg + size_t(j) * rowk)) : u32x4_t{0, 0, 0, 0};
-      vw[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vg + size_t(j) * rowk)) : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int j = jb + GROUPS * u;
-      if (j >= jend) break;  // uniform within the 16-lane group
-      float kx[8];
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    u32x4_t w = {0, 0, 0, 0};
+    if (kl < G) w = *reinterpret_cast<const u32x4_t*>(qg + size_t(kl) * D + 8 * kg + 32 * ks);
+    qloc[ks] = w;
+    if (MODE == kBifocal) {
+      u32x4_t y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kx[2 * e] = bf16_lo(kw[u][e]);
-        kx[2 * e + 1] = bf16_hi(kw[u][e]);
+        const int pi = 4 * kg + 16 * ks + e;
+        float sn, cs, y0, y1;
+        rope_sincos(dq, a.f.lo[pi], a.f.hi[pi], sn, cs);
+        rot_pair(bf16_lo(w[e]), bf16_hi(w[e]), cs, sn, y0, y1);
+        y[e] = pack_bf16(y0, y1);
       }
-      const int dist = pq - j;
-      bool remote = false;
-      bool keep = true;
-      if (MODE == kBifocal) {
-        remote = dist > w0;
-      } else if (w0 >= 0) {
-        keep = dist <= w0;
+      qrem[ks] = y;
+    }
+  }
+  // the pair frequencies of the dims this lane loads (pairs 4kg + 16ks + e)
+  uint32_t flo[KSTEPS][4], fhi[KSTEPS][4];
+  if (MODE == kBifocal) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        flo[ks][e] = a.f.lo[4 * kg + 16 * ks + e];
+        fhi[ks][e] = a.f.hi[4 * kg + 16 * ks + e];
       }
-      if (remote) {
+  }
+
+  const uint32_t rowk_b = uint32_t(a.Hkv) * D * 2;
+  const size_t bofs = size_t(b) * a.Lmax * a.Hkv * D + size_t(kvh) * D;
+  const uint32_t span = uint32_t(jend) * rowk_b;  // loads at or past jend read 0
+  const __amdgpu_buffer_rsrc_t kres = make_rsrc(static_cast<const uint16_t*>(a.k) + bofs, span);
+  const __amdgpu_buffer_rsrc_t vres = make_rsrc(static_cast<const uint16_t*>(a.v) + bofs, span);
+
+  // this wave's keys
+  const int per_wave = kDecodeChunk / WAVES;
+  const int wbeg = jbeg + wave * per_wave;
+  const int wend = min(jend, wbeg + per_wave);
+
+  u32x4_t kraw[2][KSTEPS], vraw[VPL];
+  auto load_step = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        kraw[blk][ks] = bload16(kres, uint32_t(j0 + 16 * blk + kl) * rowk_b + (8 * kg + 32 * ks) * 2);
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int c = lane + 64 * u;  // chunk c: key c / (D/8), 16-byte column c % (D/8)
+      vraw[u] = bload16(vres, uint32_t(j0 + c / (D / 8)) * rowk_b + (c % (D / 8)) * 16);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;  // per head kl (replicated over the 4 lane groups)
+  f32x4_t oacc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint16_t* vt = vtile[wave];
+  const int trow = 4 * kg + (kl >> 2);  // transposing-read row of this lane (block 0)
+  const int tcol = 4 * (kl & 3);        // and column offset within a 16-dim block
+
+  if (wbeg < wend) load_step(wbeg);
+  for (int j0 = wbeg; j0 < wend; j0 += kStep) {
+    // -- V of this step to LDS (row-major); read back transposed after the scores
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int c = lane + 64 * u;
+      *reinterpret_cast<u32x4_t*>(&vt[(c / (D / 8)) * VROW + (c % (D / 8)) * 8]) = vraw[u];
+    }
+    // -- scores S^T (keys x heads) for the two 16-key blocks
+    f32x4_t sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int jb = j0 + 16 * blk;  // first key of the block
+      // bifocal: does the block hold remote keys (pq - j > w0), local ones, or both?
+      const bool any_remote = MODE == kBifocal && (pq - jb > w0);
+      const bool any_local = MODE != kBifocal || (pq - (jb + 15) <= w0);
+      f32x4_t srem = {0.f, 0.f, 0.f, 0.f}, sloc = {0.f, 0.f, 0.f, 0.f};
+      if (any_local) {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) sloc = mfma16x16x32(kraw[blk][ks], qloc[ks], sloc);
+      }
+      if (any_remote) {
+        const int j = jb + kl;  // this lane's key
         const int dk = static_cast<int>(fastdiv(static_cast<uint32_t>(j), a.scale_div)) - j;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s, cs, y0, y1;
-          rope_sincos(dk, flo[e], fhi[e], s, cs);
-          rot_pair(kx[2 * e], kx[2 * e + 1], cs, s, y0, y1);
-          kx[2 * e] = y0;
-          kx[2 * e + 1] = y1;
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          u32x4_t y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sn, cs, y0, y1;
+            rope_sincos(dk, flo[ks][e], fhi[ks][e], sn, cs);
+            rot_pair(bf16_lo(kraw[blk][ks][e]), bf16_hi(kraw[blk][ks][e]), cs, sn, y0, y1);
+            y[e] = pack_bf16(y0, y1);
+          }
+          srem = mfma16x16x32(y, qrem[ks], srem);
         }
       }
-      float vx[8];
+      // lane l holds S^T[key jb + 4kg + i][head kl]; route, mask and scale
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vx[2 * e] = bf16_lo(vw[u][e]);
-        vx[2 * e + 1] = bf16_hi(vw[u][e]);
+      for (int i = 0; i < 4; ++i) {
+        const int j = jb + 4 * kg + i;
+        const int dist = pq - j;
+        float v;
+        if (MODE == kBifocal)
+          v = dist > w0 ? srem[i] : sloc[i];
+        else
+          v = sloc[i];
+        const bool keep = j < wend && (MODE == kBifocal || w0 < 0 || dist <= w0);
+        sc[blk][i] = keep ? v * sl2 : -INFINITY;
       }
+    }
+    // prefetch the next step while this one is processed
+    if (j0 + kStep < wend) load_step(j0 + kStep);
+
+    // -- online softmax per head over the 32 keys
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = xgroup_max(mx);
+    const float mnew = fmaxf(m_run, mx);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
+    m_run = mnew;
+    float pv[8], rs = 0.f;
 #pragma unroll
-      for (int g = 0; g < GM; ++g) {
-        if (g >= G) break;
-        float part = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sc[0][i] - mref);
+      pv[4 + i] = __builtin_amdgcn_exp2f(sc[1][i] - mref);
+      rs += pv[i] + pv[4 + i];
+    }
+    l_run = l_run * alpha + rs;
+    // P as the A operand: lane (head kl, group kg) k-slots 8kg + e are keys
+    // 4kg + e (block 0) and 16 + 4kg + e - 4 (block 1): exactly its registers
+    const u32x4_t pop = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                         pack_bf16(pv[6], pv[7])};
+    // O rows are heads 4kg + i: rescale by those heads' alpha (held by lanes kl = 4kg + i)
+    float arow[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part = fmaf(remote ? qr[g][e] : ql[g][e], kx[e], part);
-        const float sc = keep ? group_sum<LPK>(part) * sl2 : -INFINITY;
-        const float mnew = fmaxf(m_run[g], sc);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - mref);
-        const float pv = __builtin_amdgcn_exp2f(sc - mref);
-        m_run[g] = mnew;
-        l_run[g] = fmaf(l_run[g], alpha, pv);
+    for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * kg + i, 16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(o[g][e], alpha, pv * vx[e]);
-      }
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[db][i] *= arow[i];
+    // -- O += P V: V^T operand rows (keys) 4kg..4kg+3 and 16+4kg.., column kl of each 16-dim block
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const u32x2_t va = lds_read_tr16(&vt[trow * VROW + 16 * db + tcol]);
+      const u32x2_t vb = lds_read_tr16(&vt[(trow + 16) * VROW + 16 * db + tcol]);
+      oacc[db] = mfma16x16x32(pop, u32x4_t{va[0], va[1], vb[0], vb[1]}, oacc[db]);
     }
   }
 
-  // merge the lane groups' partials
-#pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    if (g >= G) break;
-    if (c == 0) {
-      red_m[grp][g] = m_run[g];
-      red_l[grp][g] = l_run[g];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red_o[grp][g][c * 8 + e] = o[g][e];
+  // ---- merge the 4 waves' partials ------------------------------------------
+  // lane (kl, kg=0) owns head kl's m and l; O[head 4kg + i][dim 16db + kl]
+  const float l_all = xgroup_sum(l_run);  // all lanes active for the cross-lane exchange
+  if (kg == 0) {
+    red_m[wave][kl] = m_run;
+    red_l[wave][kl] = l_all;
   }
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red_o[wave][4 * kg + i][16 * db + kl] = oacc[db][i];
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += kDThreads) {
     const int g = idx / D, dd = idx % D;
     float M = -INFINITY;
-    for (int r = 0; r < GROUPS; ++r) M = fmaxf(M, red_m[r][g]);
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, red_m[w][g]);
     const float Mref = M == -INFINITY ? 0.f : M;
     float acc = 0.f, lsum = 0.f;
-    for (int r = 0; r < GROUPS; ++r) {
-      const float w = __builtin_amdgcn_exp2f(red_m[r][g] - Mref);
-      acc = fmaf(w, red_o[r][g][dd], acc);
-      lsum = fmaf(w, red_l[r][g], lsum);
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(red_m[w][g] - Mref);
+      acc = fmaf(wt, red_o[w][g][dd], acc);
+      lsum = fmaf(wt, red_l[w][g], lsum);
     }
     float* dst = wsb + size_t(g) * head_stride;
     dst[2 + dd] = acc;
@@ -269,9 +373,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a)
     a.lse[size_t(b) * a.Hq + h] = lsum > 0.f ? (M + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
 }
 
-template <int D, int MODE, int GM>
+template <int D, int MODE>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, MODE, GM>), dim3(a.n_chunks, a.Hkv, a.B), dim3(kDThreads), 0,
+  hipLaunchKernelGGL((decode_split_kernel<D, MODE>), dim3(a.n_chunks, a.Hkv, a.B), dim3(kDThreads), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -279,28 +383,20 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int MODE>
-hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream) {
-  if (a.G <= 1) return launch_d<D, MODE, 1>(a, stream);
-  if (a.G <= 2) return launch_d<D, MODE, 2>(a, stream);
-  if (a.G <= 4) return launch_d<D, MODE, 4>(a, stream);
-  return launch_d<D, MODE, 8>(a, stream);
-}
-
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   if (a.D == 128) {
     switch (a.mode) {
-      case kNope: return launch_dg<128, kNope>(a, stream);
-      case kRope: return launch_dg<128, kRope>(a, stream);
-      default: return launch_dg<128, kBifocal>(a, stream);
+      case kNope: return launch_d<128, kNope>(a, stream);
+      case kRope: return launch_d<128, kRope>(a, stream);
+      default: return launch_d<128, kBifocal>(a, stream);
     }
   }
   switch (a.mode) {
-    case kNope: return launch_dg<64, kNope>(a, stream);
-    case kRope: return launch_dg<64, kRope>(a, stream);
-    default: return launch_dg<64, kBifocal>(a, stream);
+    case kNope: return launch_d<64, kNope>(a, stream);
+    case kRope: return launch_d<64, kRope>(a, stream);
+    default: return launch_d<64, kBifocal>(a, stream);
   }
 }
 

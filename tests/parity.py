@@ -92,7 +92,10 @@ def gpu_decode(inputs, **kw):
 
 
 def oracle_decode(inputs, mode, **kw):
+    """Decode oracle; the remote view's rotated q and k enter the score rounded to
+    bf16, as they do on the GPU's bf16 MFMA (same contract as prefill)."""
     kw = dict(kw)
+    kw.setdefault("operand_round", "bf16")
     if kw.get("softmax_scale", 0.0) == 0.0:
         kw.pop("softmax_scale", None)
     return O.decode_ref(to_np(inputs["q"]), to_np(inputs["k_cache"]), to_np(inputs["v_cache"]),

@@ -101,7 +101,8 @@ def _decode(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, kv_len=FAKE, B=1, Lmax=4096, Hq=32
     (dict(q=None), INVALID), (dict(kv_len=None), INVALID), (dict(ws=None), INVALID),
     (dict(Lmax=0), INVALID), (dict(Hq=30, Hkv=8), INVALID), (dict(d=80), INVALID),
     (dict(params=_params(mode=P.ROPE, remap_scale=1, period=16)), INVALID),
-    (dict(dt=1), UNSUPPORTED), (dict(Hq=64, Hkv=4), UNSUPPORTED),
+    (dict(dt=1), UNSUPPORTED), (dict(Hq=64, Hkv=2), UNSUPPORTED),
+    (dict(Lmax=1 << 21, Hkv=8, Hq=32), UNSUPPORTED),
     (dict(ws_bytes=100), WORKSPACE),
 ])
 def test_decode_rejects(kw, code):

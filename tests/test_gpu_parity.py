@@ -170,7 +170,7 @@ def test_decode_matches_prefill_last_row():
     o_dec = P.decode(ql, kc, v, torch.tensor([S], dtype=torch.int32).cuda(), mode="bifocal", **kw)
     torch.cuda.synchronize()
     # the decode oracle on the exact same (rounded) cache and query
-    ref, _ = O.decode_ref(to_np(ql), to_np(kc), to_np(v), [S], "bifocal", **kw)
+    ref, _ = O.decode_ref(to_np(ql), to_np(kc), to_np(v), [S], "bifocal", operand_round="bf16", **kw)
     assert_close(to_np(o_dec), ref, "bf16", "decode vs oracle on rope_apply cache")
     # and the direct prefill oracle's last row (the Eq. (4)-(6) identity), bf16 cache rounding included
     o_pre, _ = O.prefill_ref(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), inp["pos"].numpy(),
