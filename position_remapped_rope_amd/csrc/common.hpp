@@ -23,19 +23,29 @@ struct RopeFreq {
   uint32_t hi[kMaxPairs];
 };
 
-// Top 32 bits of (r * F) mod 2^64 as a signed fraction of a turn.
-// Works for negative r (two's complement sign extension of r to 64 bits).
-__device__ __forceinline__ float phase_turns(int32_t r, uint32_t flo, uint32_t fhi) {
+// Top 32 bits of (r * F) mod 2^64: the phase in units of 2^-32 turn. Works for
+// negative r (two's complement sign extension of r to 64 bits).
+__device__ __forceinline__ uint32_t phase_top(int32_t r, uint32_t flo, uint32_t fhi) {
   const uint32_t ru = static_cast<uint32_t>(r);
   uint32_t top = __umulhi(ru, flo) + ru * fhi;
   if (r < 0) top -= flo;
-  return static_cast<float>(static_cast<int32_t>(top)) * 0x1p-32f;
+  return top;
 }
 
 // sin and cos of 2*pi*t for t in [-1/2, 1/2) (v_sin_f32 / v_cos_f32 take revolutions).
 __device__ __forceinline__ void sincos_turns(float t, float& s, float& c) {
   s = __builtin_amdgcn_sinf(t);
   c = __builtin_amdgcn_cosf(t);
+}
+
+// The same phase as a signed fraction of a turn in [-1/2, 1/2).
+__device__ __forceinline__ float phase_turns(int32_t r, uint32_t flo, uint32_t fhi) {
+  return static_cast<float>(static_cast<int32_t>(phase_top(r, flo, fhi))) * 0x1p-32f;
+}
+
+// sin/cos of a phase held as 2^-32 turn units
+__device__ __forceinline__ void phase_sincos(uint32_t ph, float& s, float& c) {
+  sincos_turns(static_cast<float>(static_cast<int32_t>(ph)) * 0x1p-32f, s, c);
 }
 
 __device__ __forceinline__ void rope_sincos(int32_t r, uint32_t flo, uint32_t fhi, float& s,

@@ -131,16 +131,35 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
       qrem[ks] = y;
     }
   }
-  // the pair frequencies of the dims this lane loads (pairs 4kg + 16ks + e)
-  uint32_t flo[KSTEPS][4], fhi[KSTEPS][4];
+  // ---- remote-key rotation phases ------------------------------------------
+  // Lane l rotates key j (block 0) and key j + 16 (block 1) of each step, for
+  // its pairs 4kg + 16ks + e. When s divides 16, dk_j = floor(j/s) - j moves
+  // by d16 = 16/s - 16 between those keys and by 2*d16 from step to step, so
+  // each pair's phase (2^-32 turn units) advances by a fixed increment; the
+  // carries dropped from the low 32 bits cost at most 2^-32 turn per step.
+  // Otherwise every phase is formed exactly from the frequency table in LDS.
+  __shared__ uint2 ftab[D / 2];
+  const int sdiv = static_cast<int>(a.scale_div.div);
+  const bool affine = (16 % sdiv) == 0;
+  uint32_t ph[KSTEPS][4], inc[KSTEPS][4];
+  // this wave's keys
+  const int per_wave = kDecodeChunk / WAVES;
+  const int wbeg = jbeg + wave * per_wave;
+  const int wend = min(jend, wbeg + per_wave);
   if (MODE == kBifocal) {
+    if (tid < D / 2) ftab[tid] = make_uint2(a.f.lo[tid], a.f.hi[tid]);
+    const int j = wbeg + kl;
+    const int dk0 = static_cast<int>(fastdiv(static_cast<uint32_t>(j), a.scale_div)) - j;
+    const int d16 = affine ? 16 / sdiv - 16 : 0;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        flo[ks][e] = a.f.lo[4 * kg + 16 * ks + e];
-        fhi[ks][e] = a.f.hi[4 * kg + 16 * ks + e];
+        const int pi = 4 * kg + 16 * ks + e;
+        ph[ks][e] = phase_top(dk0, a.f.lo[pi], a.f.hi[pi]);
+        inc[ks][e] = phase_top(d16, a.f.lo[pi], a.f.hi[pi]);
       }
+    __syncthreads();
   }
 
   const uint32_t rowk_b = uint32_t(a.Hkv) * D * 2;
@@ -148,11 +167,6 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const uint32_t span = uint32_t(jend) * rowk_b;  // loads at or past jend read 0
   const __amdgpu_buffer_rsrc_t kres = make_rsrc(static_cast<const uint16_t*>(a.k) + bofs, span);
   const __amdgpu_buffer_rsrc_t vres = make_rsrc(static_cast<const uint16_t*>(a.v) + bofs, span);
-
-  // this wave's keys
-  const int per_wave = kDecodeChunk / WAVES;
-  const int wbeg = jbeg + wave * per_wave;
-  const int wend = min(jend, wbeg + per_wave);
 
   u32x4_t kraw[2][KSTEPS], vraw[VPL];
   auto load_step = [&](int j0) __attribute__((always_inline)) {
@@ -199,14 +213,21 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
       }
       if (any_remote) {
         const int j = jb + kl;  // this lane's key
-        const int dk = static_cast<int>(fastdiv(static_cast<uint32_t>(j), a.scale_div)) - j;
+        const int dk = affine ? 0 : static_cast<int>(fastdiv(static_cast<uint32_t>(j), a.scale_div)) - j;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           u32x4_t y;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
+            uint32_t phk;
+            if (affine) {
+              phk = blk ? ph[ks][e] + inc[ks][e] : ph[ks][e];
+            } else {
+              const uint2 f = ftab[4 * kg + 16 * ks + e];
+              phk = phase_top(dk, f.x, f.y);
+            }
             float sn, cs, y0, y1;
-            rope_sincos(dk, flo[ks][e], fhi[ks][e], sn, cs);
+            phase_sincos(phk, sn, cs);
             rot_pair(bf16_lo(kraw[blk][ks][e]), bf16_hi(kraw[blk][ks][e]), cs, sn, y0, y1);
             y[e] = pack_bf16(y0, y1);
           }
@@ -229,6 +250,12 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
     }
     // prefetch the next step while this one is processed
     if (j0 + kStep < wend) load_step(j0 + kStep);
+    if (MODE == kBifocal && affine) {  // the lane's block-0 key moves by 32
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ph[ks][e] += 2 * inc[ks][e];
+    }
 
     // -- online softmax per head over the 32 keys
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),

@@ -50,7 +50,7 @@ struct DecodeArgs {
   RopeFreq f;
 };
 
-constexpr int kDecodeChunk = 512;  // keys per split-K chunk
+constexpr int kDecodeChunk = 2048;  // keys per split-K chunk (512 per wave)
 
 // Fill F_i = round(theta_i / (2 pi) * 2^64), theta_i = base^(-2i/d), in long double.
 void fill_rope_freq(RopeFreq& f, int d, double base);
