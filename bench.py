@@ -139,6 +139,21 @@ def bench_decode(name, steps, warmup):
     return dict(ms=ms, avg_ms=avg, bytes=kv_bytes, gbs=gbs, frac=gbs / PEAK_HBM_GBS, copies=copies)
 
 
+def bench_copy(steps, warmup, nbytes=1 << 30):
+    """A plain streaming copy of known size (y = 1 * x, fp32, torch's elementwise kernel):
+    the yardstick that converts the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    x = torch.randn(nbytes // 4, device="cuda:0")
+    y = torch.empty_like(x)
+
+    def step(_):
+        torch.mul(x, 1.0, out=y)
+
+    ms, wall = time_launches(step, steps, warmup)
+    avg = sum(ms) / len(ms)
+    return dict(avg_ms=avg, read_bytes=nbytes, write_bytes=nbytes, gbs=2 * nbytes / (avg * 1e-3) / 1e9)
+
+
 def cpu_baseline(w, inp, n_rows: int):
     """The fp64 oracle, as it stands, on a bounded sample of query rows of the same workload."""
     import numpy as np
@@ -170,8 +185,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=96)
-    ap.add_argument("--only", choices=["prefill_64k", "prefill_128k", "decode_b1", "decode_b8"],
+    ap.add_argument("--cpu-rows", type=int, default=640)
+    ap.add_argument("--only", choices=["prefill_64k", "prefill_128k", "decode_b1", "decode_b8", "copy"],
                     help="time one leg only and print its figures (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -184,7 +199,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     if args.only:
-        if args.only.startswith("prefill"):
+        if args.only == "copy":
+            name = "copy_1GiB_fp32"
+            r = bench_copy(args.steps, args.warmup)
+        elif args.only.startswith("prefill"):
             name = "bifocal_64k" if args.only == "prefill_64k" else "bifocal_128k"
             _, _, r = bench_prefill(name, args.steps, args.warmup)
             r.pop("ms")
