@@ -10,9 +10,9 @@
 //
 // Work decomposition. A workgroup (8 wavefronts, two per SIMD) owns 256 query
 // rows: HG query heads of one KV group times BMp = 256/HG consecutive
-// positions. Each wave owns 32 rows = 32 positions of one head. All query heads that read the same KV
-// head sit in one workgroup when possible (HG = 4, 2 or 1), so each K tile
-// rotated into LDS is shared by all of them.
+// positions. Each wave owns 32 rows = 32 positions of one head. All query
+// heads that read the same KV head sit in one workgroup when possible (HG = 4,
+// 2 or 1), so each K tile rotated into LDS is shared by all of them.
 //
 // Bifocal merge. The workgroup walks the remote keys first (queries and keys
 // rotated at floor(p/s)), then the local window (rotated at p), carrying one
@@ -25,12 +25,19 @@
 //
 // MFMA layout (32x32x16, bf16): S^T = K Q^T, so a lane's output column is a
 // query row: lane l holds row m = l % 32 and keys n = 8*(r/4) + 4*(l/32) + r%4
-// of accumulator register r. The same
-// register order serves directly as the B operand of O^T += V^T P^T. V stays
-// row-major in LDS; its transposed A operand comes from ds_read_b64_tr_b16.
+// of accumulator register r. The same register order serves directly as the
+// B operand of O^T += V^T P^T. V stays row-major in LDS; its transposed A
+// operand comes from ds_read_b64_tr_b16.
 //
-// Overlap. Two waves share each SIMD; while one issues MFMAs the other's
-// vector-ALU work (exponentials, RoPE of the next K tile) can co-issue.
+// Schedule (two wave groups in antiphase). Waves 0-3 (group 0) and 4-7
+// (group 1) put one wave of each group on every SIMD. Every wave alternates a
+// matrix phase (O += P V for tile t, then S = K Q^T for tile t+1: 32 MFMAs)
+// followed by its share of the K/V staging (RoPE of K rows, LDS stores), and
+// a vector phase (mask, online softmax and P packing for tile t+1). Group 1
+// runs one phase behind group 0, and a workgroup barrier separates phases, so
+// on each SIMD one wave's MFMAs and staging overlap the other wave's softmax.
+// K and V tiles are double-buffered in LDS; each group stages half of every
+// tile's rows, with the global loads issued one phase pair ahead.
 #include <limits.h>
 
 #include "internal.hpp"
@@ -39,12 +46,14 @@ namespace prope {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 512;  // 8 wavefronts, 2 per SIMD
+constexpr int kGroupThreads = kThreads / 2;
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -82,6 +91,12 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// Sum of the two bf16 halves of a packed word, added to c (v_dot2c_f32_bf16).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float c) {
+  const bf16x2_t one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, c, false);
+}
+
 template <int MODE>
 __device__ __forceinline__ int rot_index(int p, int rot, const PrefillArgs& a) {
   if (rot == 2) return static_cast<int>(fastdiv(static_cast<uint32_t>(p), a.scale_div));
@@ -106,21 +121,23 @@ __device__ __forceinline__ u32x4_t rotate_chunk(u32x4_t x, int r, const uint32_t
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const PrefillArgs a) {
-  constexpr int KS = D / 16;            // MFMA k-steps over the head dimension
-  constexpr int DB = D / 32;            // 32-row blocks of O^T
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int RPP = kThreads / CPR;   // rows covered by one staging sweep
-  constexpr int NU = kBN / RPP;         // K (and V) chunks per thread per tile
-  constexpr int KRow = D + 8;           // K tile row stride: 16-byte reads of 8 rows hit distinct banks
-  constexpr int VRow = D + 16;          // V tile row stride: transposing reads of 4 rows hit distinct banks
-  static_assert(NU >= 1 && NU <= 2, "staging layout");
+  constexpr int KS = D / 16;                  // MFMA k-steps over the head dimension
+  constexpr int DB = D / 32;                  // 32-row blocks of O^T
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int HR = kBN / 2;                 // tile rows staged by one group
+  constexpr int RPS = kGroupThreads / CPR;    // rows covered by one staging sweep of a group
+  constexpr int NU = HR / RPS;                // K (and V) chunks per thread per tile
+  constexpr int KRow = D + 8;                 // K tile row stride: 16-byte reads of 8 rows hit distinct banks
+  constexpr int VRow = D + 32;                // V tile row stride: the 4 rows of a transposing read hit distinct banks
+  static_assert(NU >= 1 && NU <= 2 && NU * RPS == HR, "staging layout");
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KRow];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * VRow];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
   const int lr = lane & 31, lg = lane >> 5;
-  const int group = wave >> 2;  // one wave of each group per SIMD
+  const int group = wave >> 2;  // waves w and w + 4 share a SIMD
 
   // ---- work item --------------------------------------------------------
   int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -182,21 +199,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   };
 
   // ---- per-thread staging coordinates --------------------------------------
-  const int sc = tid % CPR;   // 16-byte column chunk this thread stages (K and V)
-  const int sr = tid / CPR;   // first row this thread stages (second: sr + RPP)
+  // group g stages rows [HR*g, HR*g + HR) of every K and V tile
+  const int gtid = tid & (kGroupThreads - 1);
+  const int sc = gtid % CPR;                 // 16-byte column chunk this thread stages
+  const int sr = group * HR + gtid / CPR;    // first row this thread stages (then sr + RPS)
   const uint32_t kcol_b = uint32_t(kvh) * D * 2 + sc * 16;
 
   // Per-chunk constants kept in LDS rather than registers: the 4 pair
   // frequencies of each 16-byte column chunk, and for each rotation kind the
   // cos/sin of the affine id step between the two K rows a thread stages. The
-  // second K row a thread stages is RPP keys after the first; when their
-  // rotation ids differ by that step (RPP for base ids, RPP / s for remote ids
-  // when s divides RPP) its cos/sin are the first row's times the step's.
+  // second K row a thread stages is RPS keys after the first; when their
+  // rotation ids differ by that step (RPS for base ids, RPS / s for remote ids
+  // when s divides RPS) its cos/sin are the first row's times the step's.
   __shared__ uint2 kfreq[CPR * 4];
   __shared__ float2 kstep[2][CPR * 4];
-  const int id_step1 = NU > 1 ? RPP : -1;
+  const int id_step1 = NU > 1 ? RPS : -1;
   const int sdiv = static_cast<int>(a.scale_div.div);
-  const int id_step2 = (NU > 1 && RPP % sdiv == 0) ? RPP / sdiv : -1;
+  const int id_step2 = (NU > 1 && RPS % sdiv == 0) ? RPS / sdiv : -1;
   if (MODE != kNope && tid < CPR * 4) {
     const uint32_t flo = a.f.lo[tid], fhi = a.f.hi[tid];
     kfreq[tid] = make_uint2(flo, fhi);
@@ -211,32 +230,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   u32x4_t kraw[NU], vraw[NU];
   int kid[NU];
 
-  // global -> registers: K rows of tile tk and V rows of tile tv (either may be >= T: skipped)
+  // global -> registers: this thread's K rows of tile tk and V rows of tile tv
+  // (a tile index outside [0, T) is skipped)
   auto stage_load = [&](int tk, int tv) __attribute__((always_inline)) {
-    if (tk < T) {
+    if (tk >= 0 && tk < T) {
       int p, kt;
       tile_of(tk, p, kt);
       const int rot = p ? rot1 : rot0;
       const uint32_t j0 = uint32_t(kt) * kBN;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const uint32_t j = j0 + sr + RPP * u;
+        const uint32_t j = j0 + sr + RPS * u;
         kraw[u] = bload16(kres, j * rowk_b + kcol_b);
         kid[u] = (MODE != kNope && rot) ? bload_i32(pres, j * 4) : 0;
       }
     }
-    if (tv < T) {
+    if (tv >= 0 && tv < T) {
       int p, kt;
       tile_of(tv, p, kt);
       const uint32_t j0 = uint32_t(kt) * kBN;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) vraw[u] = bload16(vres, (j0 + sr + RPP * u) * rowk_b + kcol_b);
+      for (int u = 0; u < NU; ++u) vraw[u] = bload16(vres, (j0 + sr + RPS * u) * rowk_b + kcol_b);
     }
   };
 
   // registers -> LDS: K of tile tk (rotated for its pass) and V of tile tv
   auto stage_store = [&](int tk, int tv) __attribute__((always_inline)) {
-    if (tk < T) {
+    if (tk >= 0 && tk < T) {
       int p, kt;
       tile_of(tk, p, kt);
       uint16_t* dst = Ks[tk & 1];
@@ -279,17 +299,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
             rot_pair(bf16_lo(kraw[u][e]), bf16_hi(kraw[u][e]), cs[e], sn[e], y0, y1);
             y[e] = pack_bf16(y0, y1);
           }
-          *reinterpret_cast<u32x4_t*>(&dst[(sr + RPP * u) * KRow + sc * 8]) = y;
+          *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = y;
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPP * u) * KRow + sc * 8]) = kraw[u];
+        for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = kraw[u];
       }
     }
-    if (tv < T) {
+    if (tv >= 0 && tv < T) {
       uint16_t* dst = Vs[tv & 1];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPP * u) * VRow + sc * 8]) = vraw[u];
+      for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * VRow + sc * 8]) = vraw[u];
     }
   };
 
@@ -329,6 +349,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  f32x16_t sacc[2];    // S^T of the tile in flight (two 32-key blocks)
+  u32x4_t pop[4];      // its P, bf16, as four 16-key B operands
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) pop[kk] = u32x4_t{0, 0, 0, 0};
   float m_run = -INFINITY;  // running max of scaled scores, log2 units
   float l_run = 0.f;        // this lane's share of the running sum
   const float sl2 = a.scale_log2;
@@ -344,6 +368,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     need_mask = dmin < dlo || dmax > dhi;
     return i1 >= i0 && dmax >= dlo && dmin <= dhi;
   };
+  auto live = [&](int t) __attribute__((always_inline)) {
+    bool nm;
+    int dlo, dhi, j0;
+    return wave_live(t, nm, dlo, dhi, j0);
+  };
+  auto pass_of = [&](int t) __attribute__((always_inline)) { return t < tc0 ? 0 : 1; };
 
   auto xhalf_max = [&](float x) __attribute__((always_inline)) {
     // max with the lane 32 apart (same query row, other half of the keys)
@@ -351,106 +381,136 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   };
 
-  // ---- main loop: one barrier per 64-key tile --------------------------------
-  // Iteration t issues the global loads of tile t+1, computes tile t from LDS
-  // (S^T = K Q^T, online softmax, O^T += V^T P^T), then rotates tile t+1's K
-  // into the other LDS buffer.
-  int cur_pass;
-  {
-    int p0, kt0;
-    tile_of(0, p0, kt0);
-    cur_pass = p0;
-  }
-  stage_load(0, 0);
-  stage_store(0, 0);
-  load_q(cur_pass);
-  __syncthreads();
-
-  for (int t = 0; t < T; ++t) {
-    const int buf = t & 1;
-    int p, kt;
-    tile_of(t, p, kt);
-    if (p != cur_pass) {  // first tile of the local pass: re-rotate the queries
-      cur_pass = p;
-      load_q(p);
+  // matrix phase, part 1: O^T += V^T P^T for tile t
+  auto pv_step = [&](int t) __attribute__((always_inline)) {
+    const uint16_t* vbase = &Vs[t & 1][vrow0 * VRow + vcol0];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint16_t* vrow = vbase + kk * 16 * VRow;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2_t va = lds_read_tr16(vrow + db * 32);
+        const u32x2_t vb = lds_read_tr16(vrow + 8 * VRow + db * 32);
+        const u32x4_t vop = {va[0], va[1], vb[0], vb[1]};
+        oacc[db] = mfma32x32x16(vop, pop[kk], oacc[db]);
+      }
     }
-    if (t + 1 < T) stage_load(t + 1, t + 1);
-    bool need_mask;
-    int dlo, dhi, j0;
-    if (wave_live(t, need_mask, dlo, dhi, j0)) {
-      // S^T = K Q^T for the 64 keys (two 32-key blocks nb) and the wave's 32 rows
-      f32x16_t sacc[2];
+  };
+  // matrix phase, part 2: S^T = K Q^T for tile t
+  auto qk_step = [&](int t) __attribute__((always_inline)) {
+    const uint16_t* kbase = &Ks[t & 1][lr * KRow + lg * 8];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const u32x4_t kop = *reinterpret_cast<const u32x4_t*>(kbase + nb * 32 * KRow + ks * 16);
+        sacc[nb] = mfma32x32x16(kop, qreg[ks], sacc[nb]);
+      }
+    }
+  };
+  auto qk_or_clear = [&](int t) __attribute__((always_inline)) {
+    if (t < T && live(t)) {
+      qk_step(t);
+    } else {  // nothing to score: keeps sacc from living across the whole loop
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
+    }
+  };
+
+  // vector phase of tile t: mask, online softmax, P -> bf16, lazy O rescale
+  auto softmax_step = [&](int t) __attribute__((always_inline)) {
+    bool need_mask;
+    int dlo, dhi, j0;
+    if (!wave_live(t, need_mask, dlo, dhi, j0)) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const u32x4_t kop = *reinterpret_cast<const u32x4_t*>(&Ks[buf][(nb * 32 + lr) * KRow + ks * 16 + lg * 8]);
-          sacc[nb] = mfma32x32x16(kop, qreg[ks], sacc[nb]);
-        }
-      }
-      if (need_mask) {
-        const int dbase = (i0 + lr) - (j0 + 4 * lg);  // i - j of register 0 of block 0
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int dist = dbase - (nb * 32 + 8 * (r >> 2) + (r & 3));
-            if (dist < dlo || dist > dhi) sacc[nb][r] = -INFINITY;
-          }
-      }
-      // online softmax; a lane's column is one query row
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[nb][r], sacc[nb][r + 1]));
-      mx = xhalf_max(mx);
-      const float mnew = fmaxf(m_run, mx * sl2);
-      const bool grow = mnew > m_run;
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
-      m_run = mnew;
-      float rs = 0.f;
+      for (int kk = 0; kk < 4; ++kk) pop[kk] = u32x4_t{0, 0, 0, 0};
+      return false;
+    }
+    if (need_mask) {
+      const int dbase = (i0 + lr) - (j0 + 4 * lg);  // i - j of register 0 of block 0
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], sl2, -mref));
-          sacc[nb][r] = pv;
-          rs += pv;
+          const int dist = dbase - (nb * 32 + 8 * (r >> 2) + (r & 3));
+          if (dist < dlo || dist > dhi) sacc[nb][r] = -INFINITY;
         }
-      l_run = l_run * alpha + rs;
-      if (__any(grow)) {  // rescale O only when some row of the wave raised its max
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      // O^T += V^T P^T over the 64 keys (four k-steps of 16)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int nb = kk >> 1, r0 = (kk & 1) * 8;
-        const u32x4_t pop = {pack_bf16(sacc[nb][r0 + 0], sacc[nb][r0 + 1]),
-                             pack_bf16(sacc[nb][r0 + 2], sacc[nb][r0 + 3]),
-                             pack_bf16(sacc[nb][r0 + 4], sacc[nb][r0 + 5]),
-                             pack_bf16(sacc[nb][r0 + 6], sacc[nb][r0 + 7])};
-        const uint16_t* vrow = &Vs[buf][(kk * 16 + vrow0) * VRow + vcol0];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2_t va = lds_read_tr16(vrow + db * 32);
-          const u32x2_t vb = lds_read_tr16(vrow + 8 * VRow + db * 32);
-          const u32x4_t vop = {va[0], va[1], vb[0], vb[1]};
-          oacc[db] = mfma32x32x16(vop, pop, oacc[db]);
-        }
-      }
     }
-    if (t + 1 < T) stage_store(t + 1, t + 1);
-    __syncthreads();
+    float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[1][0], sacc[1][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      mx0 = fmaxf(mx0, fmaxf(sacc[0][r], sacc[0][r + 1]));
+      mx1 = fmaxf(mx1, fmaxf(sacc[1][r], sacc[1][r + 1]));
+    }
+    const float mx = xhalf_max(fmaxf(mx0, mx1));
+    const float mnew = fmaxf(m_run, mx * sl2);
+    const bool grow = mnew > m_run;
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
+    m_run = mnew;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int nb = kk >> 1, r0 = (kk & 1) * 8;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r0 + e], sl2, -mref));
+      const u32x4_t w = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                         pack_bf16(pv[6], pv[7])};
+      pop[kk] = w;
+      // the row sum takes the same bf16 P the PV product uses
+      rs0 = add_bf16_pair(w[0], rs0);
+      rs1 = add_bf16_pair(w[1], rs1);
+      rs0 = add_bf16_pair(w[2], rs0);
+      rs1 = add_bf16_pair(w[3], rs1);
+    }
+    l_run = l_run * alpha + (rs0 + rs1);
+    if (__any(grow)) {  // rescale O only when some row of the wave raised its max
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    return true;
+  };
+
+  // ---- prologue: K tile 0 in LDS; K tile 1 and V tile 0 in registers --------
+  stage_load(0, -1);
+  stage_store(0, -1);
+  stage_load(1, 0);
+  load_q(pass_of(0));
+  lds_barrier();
+
+  // ---- phases -----------------------------------------------------------------
+  // Group 0: QK(0) | soft(0) | PV(0) QK(1) | soft(1) | PV(1) QK(2) | ... | PV(T-1) | -
+  // Group 1:  -    | QK(0)   | soft(0)     | PV(0) QK(1) | ...         | PV(T-1)
+  // with a workgroup barrier after every phase. After its MFMAs for tile t
+  // (PV(t), QK(t+1)) a wave stores its half of K tile t+2 and V tile t+1 to
+  // LDS and issues the loads of K tile t+3 and V tile t+2, so the RoPE work
+  // of the staging runs while the other wave of the SIMD is in its softmax.
+  if (group == 1) lds_barrier();
+  qk_or_clear(0);
+  stage_store(1, 0);
+  stage_load(2, 1);
+  lds_barrier();
+#pragma clang loop unroll(disable)
+  for (int t = 0; t < T; ++t) {
+    const bool lv = softmax_step(t);
+    if (MODE == kBifocal && t + 1 < T && pass_of(t + 1) != pass_of(t)) load_q(pass_of(t + 1));
+    lds_barrier();
+    if (lv) pv_step(t);
+    qk_or_clear(t + 1);
+    stage_store(t + 2, t + 1);
+    stage_load(t + 3, t + 2);
+    lds_barrier();
   }
+  if (group == 0) lds_barrier();
 
   // ---- finalize ---------------------------------------------------------------
   uint16_t* og = static_cast<uint16_t*>(a.o) + size_t(b) * S * a.Hq * D + size_t(h) * D;
