@@ -143,6 +143,12 @@ DEC_SMALL = [
     ("nope_window", (2, 1030, 4, 1, 128), "nope", dict(window_left=100), [1030, 40]),
     ("rope_full", (1, 600, 16, 2, 128), "rope", dict(rope_base=1e4), [600]),
     ("gqa3", (1, 900, 6, 2, 128), "bifocal", dict(rope_base=1e6, remap_scale=2, window_left=50), [900]),
+    # several 2048-key chunks per sequence, lengths on and next to chunk edges
+    ("multi_chunk_ragged", (4, 6200, 8, 2, 128), "bifocal", dict(rope_base=1e6, remap_scale=4, window_left=2500),
+     [6200, 2048, 2049, 4097]),
+    ("multi_chunk_s3_d64", (2, 4500, 16, 4, 64), "bifocal", dict(rope_base=1e6, remap_scale=3, window_left=1000),
+     [4500, 4096]),
+    ("multi_chunk_nope_window", (1, 5000, 8, 8, 128), "nope", dict(window_left=2100), [5000]),
 ]
 
 
@@ -157,6 +163,28 @@ def test_decode_small(name, shape, mode, kw, lens):
     o_ref, lse_ref = oracle_decode(inp, mode, **kw)
     assert_close(to_np(o), o_ref, "bf16", name)
     assert float(np.max(np.abs(lse.cpu().numpy() - lse_ref))) < LSE_TOL["bf16"]
+
+
+def test_decode_workspace_reuse():
+    """One workspace serves consecutive calls with other lengths: each result is
+    bit-identical to a call with a fresh workspace (no state survives a call)."""
+    B, L, Hq, Hkv, d = 2, 5000, 8, 2, 128
+    w = W.Workload("t", "decode", B=B, S=L, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", mode="bifocal",
+                   rope_base=1e6, seed=404)
+    inp = W.make_decode_inputs(w)
+    dev = torch.device("cuda:0")
+    q, kc, vc = (inp[n].to(dev) for n in ("q", "k_cache", "v_cache"))
+    kw = dict(rope_base=1e6, remap_scale=2, window_left=700)
+    ws = torch.full((P.decode_workspace_size(B, L, Hq, d),), 0x7f, dtype=torch.uint8, device=dev)
+    for lens in ([5000, 3000], [1, 4097], [5000, 5000], [2048, 2049]):
+        kv_len = torch.tensor(lens, dtype=torch.int32, device=dev)
+        o_reuse = P.decode(q, kc, vc, kv_len, mode="bifocal", workspace=ws, **kw)
+        o_fresh = P.decode(q, kc, vc, kv_len, mode="bifocal", **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o_reuse, o_fresh), lens
+    sub = dict(inp, kv_len=torch.tensor([2048, 2049], dtype=torch.int32))
+    o_ref, _ = oracle_decode(sub, "bifocal", **kw)
+    assert_close(to_np(o_reuse), o_ref, "bf16", "reused workspace vs oracle")
 
 
 def test_decode_matches_prefill_last_row():
