@@ -448,8 +448,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       mx0 = fmaxf(mx0, fmaxf(sacc[0][r], sacc[0][r + 1]));
       mx1 = fmaxf(mx1, fmaxf(sacc[1][r], sacc[1][r + 1]));
     }
-    const float mx = xhalf_max(fmaxf(mx0, mx1));
-    const float mnew = fmaxf(m_run, mx * sl2);
+    const float mx = xhalf_max(fmaxf(mx0, mx1)) * sl2;
+    // The reference max moves only when the tile's max exceeds it by more than
+    // 8 (log2 units): P <= 2^8 stays exact in bf16 and fp32, and O and l are
+    // rescaled far less often. The final O / l and LSE = m + log2 l are unchanged.
+    const float mnew = mx > m_run + 8.f ? mx : m_run;
     const bool grow = mnew > m_run;
     const float mref = mnew == -INFINITY ? 0.f : mnew;
     const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
