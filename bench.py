@@ -84,7 +84,7 @@ def time_launches(fn, steps: int, warmup: int):
     return ms, wall
 
 
-def bench_prefill(name, steps, warmup):
+def bench_prefill(name, steps, warmup, unfused=False):
     import torch
     import position_remapped_rope_amd as P
     import workloads as W
@@ -96,10 +96,16 @@ def bench_prefill(name, steps, warmup):
     o = torch.empty_like(q)
     kw = dict(rope_base=w.rope_base, remap_scale=w.remap_scale, window_left=w.window_left)
 
-    def step(_):
-        P.prefill(q, k, v, pos, mode="bifocal", out=o, **kw)
+    if unfused:  # the pages' three-call construction merged by Eq. (7), for comparison
+        ws = torch.empty(P.bifocal_unfused_workspace_size(w.B, w.S, w.Hq, w.d), dtype=torch.uint8, device=dev)
 
-    log(f"{name}: timing {steps} launches")
+        def step(_):
+            P.prefill_bifocal_unfused(q, k, v, pos, out=o, workspace=ws, **kw)
+    else:
+        def step(_):
+            P.prefill(q, k, v, pos, mode="bifocal", out=o, **kw)
+
+    log(f"{name}: timing {steps} launches" + (" (unfused)" if unfused else ""))
     ms, wall = time_launches(step, steps, warmup)
     flops = prefill_flops(w)
     avg = sum(ms) / len(ms)
@@ -186,7 +192,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=640)
-    ap.add_argument("--only", choices=["prefill_64k", "prefill_128k", "decode_b1", "decode_b8", "copy"],
+    ap.add_argument("--only", choices=["prefill_64k", "prefill_128k", "prefill_64k_unfused", "decode_b1", "decode_b8", "copy"],
                     help="time one leg only and print its figures (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -203,8 +209,8 @@ def main():
             name = "copy_1GiB_fp32"
             r = bench_copy(args.steps, args.warmup)
         elif args.only.startswith("prefill"):
-            name = "bifocal_64k" if args.only == "prefill_64k" else "bifocal_128k"
-            _, _, r = bench_prefill(name, args.steps, args.warmup)
+            name = "bifocal_128k" if args.only == "prefill_128k" else "bifocal_64k"
+            _, _, r = bench_prefill(name, args.steps, args.warmup, unfused=args.only.endswith("unfused"))
             r.pop("ms")
         else:
             name = "bifocal_decode_128k_b1" if args.only == "decode_b1" else "bifocal_decode_128k_b8"
@@ -242,6 +248,10 @@ def main():
         w4, _, pre4 = bench_prefill("bifocal_128k", max(3, args.steps // 2), 1)
         extra["bifocal_128k"] = {"tflops": round(pre4["tflops"], 2), "frac_bf16_peak": round(pre4["frac"], 4),
                                  "avg_ms": round(pre4["avg_ms"], 3), "flop": pre4["flops"]}
+        torch.cuda.empty_cache()
+        _, _, unf = bench_prefill("bifocal_64k", max(3, args.steps // 2), 1, unfused=True)
+        extra["bifocal_64k_unfused_eq7"] = {"tflops": round(unf["tflops"], 2), "avg_ms": round(unf["avg_ms"], 3),
+                                            "fused_speedup": round(unf["avg_ms"] / pre["avg_ms"], 3)}
         for name, st in (("bifocal_decode_128k_b1", 50), ("bifocal_decode_128k_b8", 10)):
             d = bench_decode(name, st, 3)
             extra[name] = {"gbs": round(d["gbs"], 1), "frac_hbm_peak": round(d["frac"], 4),

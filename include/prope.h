@@ -97,6 +97,32 @@ int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, flo
                        const prope_params* params, void* stream);
 
 /*
+ * Bifocal prefill composed as the pages' unfused construction (Jet-Long
+ * "Efficient Long-Context Extension with Dynamic Bifocal RoPE", section 3.3,
+ * Eq. (7)): three ordinary attention calls, each returning O_X and its LSE,
+ *   A: window i - j <= w0 at the ids pos,
+ *   B: full causal attention at the remote ids floor(pos / s),
+ *   C: window i - j <= w0 at the remote ids,
+ * merged per query row in fp32 as
+ *   (W_A O_A + W_B O_B - W_C O_C) / (W_A + W_B - W_C), W_X = exp(l_X - max l).
+ * Same result as prope_attn_prefill in BIFOCAL mode up to rounding (each call
+ * rounds its O_X to dt); provided to measure the fused kernel against the
+ * construction it replaces and to check Eq. (7) on the device.
+ *   Arguments as prope_attn_prefill; params->mode must be PROPE_BIFOCAL and
+ *   pos is required (ids >= 0).
+ *   workspace: caller-owned device buffer, 256-byte aligned, of at least
+ *     prope_bifocal_unfused_workspace_size(B, S, Hq, d, dt) bytes (O_A, O_C,
+ *     three LSE vectors, remote ids); too small -> PROPE_ERR_WORKSPACE. Its
+ *     contents need no initialisation and are scratch after the call.
+ *   Enqueues five kernels on `stream`.
+ */
+size_t prope_bifocal_unfused_workspace_size(int B, int S, int Hq, int d, int dt);
+int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
+                                       const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int dt,
+                                       const prope_params* params, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
  * Decode: one new query token per sequence against a KV cache.
  *   q [B,Hq,d]: the new token's query ALREADY rotated at its own position
  *     kv_len[b]-1 (the base view, Jet-Long Eq. (6)'s q_local).

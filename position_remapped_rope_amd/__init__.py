@@ -12,13 +12,15 @@ import os
 from typing import Optional
 
 __all__ = ["NOPE", "ROPE", "BIFOCAL", "PropeError", "lib", "lib_path", "rope_apply", "prefill",
-           "decode", "decode_workspace_size", "group_size", "status_string", "EXPORTED_SYMBOLS"]
+           "prefill_bifocal_unfused", "bifocal_unfused_workspace_size", "decode", "decode_workspace_size",
+           "group_size", "status_string", "EXPORTED_SYMBOLS"]
 
 NOPE, ROPE, BIFOCAL = 0, 1, 2
 _MODES = {"nope": NOPE, "rope": ROPE, "bifocal": BIFOCAL}
 BF16, FP32 = 0, 1
 
-EXPORTED_SYMBOLS = ("prope_attn_prefill", "prope_attn_decode", "prope_decode_workspace_size",
+EXPORTED_SYMBOLS = ("prope_attn_prefill", "prope_attn_prefill_bifocal_unfused",
+                    "prope_bifocal_unfused_workspace_size", "prope_attn_decode", "prope_decode_workspace_size",
                     "prope_rope_apply", "prope_group_size", "prope_status_string", "prope_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +57,11 @@ def lib():
     L.prope_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      ctypes.POINTER(PropeParams), vp]
     L.prope_attn_prefill.restype = i32
+    L.prope_attn_prefill_bifocal_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                     ctypes.POINTER(PropeParams), vp, ctypes.c_size_t, vp]
+    L.prope_attn_prefill_bifocal_unfused.restype = i32
+    L.prope_bifocal_unfused_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.prope_bifocal_unfused_workspace_size.restype = ctypes.c_size_t
     L.prope_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     ctypes.POINTER(PropeParams), vp, ctypes.c_size_t, vp]
     L.prope_attn_decode.restype = i32
@@ -161,6 +168,38 @@ def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
     p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale)
     _check(L.prope_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos),
                                 B, S, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def bifocal_unfused_workspace_size(B: int, S: int, Hq: int, d: int, dtype_code: int = BF16) -> int:
+    return lib().prope_bifocal_unfused_workspace_size(B, S, Hq, d, dtype_code)
+
+
+def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: int = 1, window_left: int = -1,
+                            softmax_scale: float = 0.0, out=None, lse=None, workspace=None,
+                            return_lse: bool = False):
+    """Bifocal prefill as three attention calls merged by Jet-Long Eq. (7) (see include/prope.h)."""
+    import torch
+    L = lib()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (pos, "pos"), (out, "out"), (lse, "lse"), (workspace, "workspace")):
+        _dev(t, n)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise PropeError("k and v must be [B,S,Hkv,d] with q's dtype")
+    if pos is None or pos.dtype != torch.int32 or tuple(pos.shape) != (B, S):
+        raise PropeError("pos must be int32 [B,S]")
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    need = L.prope_bifocal_unfused_workspace_size(B, S, Hq, d, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    p = _params("bifocal", rope_base, 0, remap_scale, window_left, softmax_scale)
+    _check(L.prope_attn_prefill_bifocal_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos),
+                                                B, S, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p),
+                                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                _stream(q)))
     return (o, lse) if return_lse else o
 
 

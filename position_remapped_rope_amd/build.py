@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libprope.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "rope_apply.hip", "prefill_bf16.hip", "prefill_fp32.hip", "decode_bf16.hip"]
+SOURCES = ["api.cpp", "rope_apply.hip", "prefill_bf16.hip", "prefill_fp32.hip", "decode_bf16.hip",
+           "bifocal_unfused.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

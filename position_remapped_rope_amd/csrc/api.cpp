@@ -53,6 +53,70 @@ float scale_log2(const prope_params* p, int d) {
   return static_cast<float>(s * 1.4426950408889634);  // * log2(e)
 }
 
+int check_prefill(const void* q, const void* k, const void* v, const void* o, const int32_t* pos, int B, int S,
+                  int Hq, int Hkv, int d, int dt, const prope_params* params) {
+  const int pc = check_params(params, false);
+  if (pc != PROPE_OK) return pc;
+  if (!q || !k || !v || !o) return PROPE_ERR_INVALID_ARG;
+  if (!pos && params->mode != PROPE_NOPE) return PROPE_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || (Hq % Hkv)) return PROPE_ERR_INVALID_ARG;
+  if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return PROPE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) % 16)
+    return PROPE_ERR_INVALID_ARG;
+  // one sequence's q/k/v/o slices are addressed with 32-bit byte offsets
+  if (int64_t(S) * Hq * d * 4 >= (int64_t(1) << 32)) return PROPE_ERR_UNSUPPORTED;
+  return PROPE_OK;
+}
+
+PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* pos,
+                         int B, int S, int Hq, int Hkv, int d, const prope_params& p) {
+  PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.pos = pos;
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = d;
+  a.G = Hq / Hkv;
+  a.HG = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
+  a.BMp = 256 / a.HG;
+  a.n_pblocks = (S + a.BMp - 1) / a.BMp;
+  a.n_hsub = a.G / a.HG;
+  a.mode = p.mode;
+  a.period = p.period;
+  a.window_left = p.window_left;
+  a.period_div = make_fastdiv(p.period > 0 ? static_cast<uint32_t>(p.period) : 1u);
+  a.scale_div = make_fastdiv(static_cast<uint32_t>(p.remap_scale));
+  a.scale_log2 = scale_log2(&p, d);
+  fill_rope_freq(a.f, d, p.mode == PROPE_NOPE ? 10000.0 : p.rope_base);
+  return a;
+}
+
+int run_prefill(const PrefillArgs& a, int dt, void* stream) {
+  const hipError_t e = dt == PROPE_BF16 ? launch_prefill_bf16(a, static_cast<hipStream_t>(stream))
+                                        : launch_prefill_fp32(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PROPE_OK : PROPE_ERR_HIP;
+}
+
+// Workspace of the unfused composition: O_A and O_C in the input dtype, the
+// three LSE vectors and the remote ids, each region 256-byte aligned. O_B is
+// written into the caller's output.
+struct UnfusedLayout {
+  size_t oa, oc, la, lb, lc, ids, total;
+};
+UnfusedLayout unfused_layout(int B, int S, int Hq, int d, int dt) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t obytes = up(size_t(B) * S * Hq * d * (dt == PROPE_BF16 ? 2 : 4));
+  const size_t lbytes = up(size_t(B) * Hq * S * sizeof(float));
+  UnfusedLayout l;
+  l.oa = 0;
+  l.oc = l.oa + obytes;
+  l.la = l.oc + obytes;
+  l.lb = l.la + lbytes;
+  l.lc = l.lb + lbytes;
+  l.ids = l.lc + lbytes;
+  l.total = l.ids + up(size_t(B) * S * sizeof(int32_t));
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -100,37 +164,60 @@ int prope_rope_apply(const void* x, void* y, const int32_t* pos, int B, int S, i
 int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                        const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int dt,
                        const prope_params* params, void* stream) {
-  const int pc = check_params(params, false);
+  const int pc = check_prefill(q, k, v, o, pos, B, S, Hq, Hkv, d, dt, params);
   if (pc != PROPE_OK) return pc;
-  if (!q || !k || !v || !o) return PROPE_ERR_INVALID_ARG;
-  if (!pos && params->mode != PROPE_NOPE) return PROPE_ERR_INVALID_ARG;
-  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || (Hq % Hkv)) return PROPE_ERR_INVALID_ARG;
-  if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return PROPE_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
-       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o)) % 16)
-    return PROPE_ERR_INVALID_ARG;
-  // one sequence's q/k/v/o slices are addressed with 32-bit byte offsets
-  if (int64_t(S) * Hq * d * 4 >= (int64_t(1) << 32)) return PROPE_ERR_UNSUPPORTED;
+  const PrefillArgs a = prefill_args(q, k, v, o, lse, pos, B, S, Hq, Hkv, d, *params);
+  return run_prefill(a, dt, stream);
+}
 
-  PrefillArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.pos = pos;
-  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = d;
-  a.G = Hq / Hkv;
-  a.HG = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
-  a.BMp = 256 / a.HG;
-  a.n_pblocks = (S + a.BMp - 1) / a.BMp;
-  a.n_hsub = a.G / a.HG;
-  a.mode = params->mode;
-  a.period = params->period;
-  a.window_left = params->window_left;
-  a.period_div = make_fastdiv(params->period > 0 ? static_cast<uint32_t>(params->period) : 1u);
-  a.scale_div = make_fastdiv(static_cast<uint32_t>(params->remap_scale));
-  a.scale_log2 = scale_log2(params, d);
-  fill_rope_freq(a.f, d, params->mode == PROPE_NOPE ? 10000.0 : params->rope_base);
-  const hipError_t e = dt == PROPE_BF16 ? launch_prefill_bf16(a, static_cast<hipStream_t>(stream))
-                                        : launch_prefill_fp32(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? PROPE_OK : PROPE_ERR_HIP;
+size_t prope_bifocal_unfused_workspace_size(int B, int S, int Hq, int d, int dt) {
+  if (B < 1 || S < 1 || Hq < 1 || d < 1 || (dt != PROPE_BF16 && dt != PROPE_FP32)) return 0;
+  return unfused_layout(B, S, Hq, d, dt).total;
+}
+
+int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
+                                       const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int dt,
+                                       const prope_params* params, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  const int pc = check_prefill(q, k, v, o, pos, B, S, Hq, Hkv, d, dt, params);
+  if (pc != PROPE_OK) return pc;
+  if (params->mode != PROPE_BIFOCAL || !pos || !workspace) return PROPE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return PROPE_ERR_INVALID_ARG;
+  const UnfusedLayout ly = unfused_layout(B, S, Hq, d, dt);
+  if (workspace_bytes < ly.total) return PROPE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* oa = ws + ly.oa;
+  void* oc = ws + ly.oc;
+  float* la = reinterpret_cast<float*>(ws + ly.la);
+  float* lb = reinterpret_cast<float*>(ws + ly.lb);
+  float* lc = reinterpret_cast<float*>(ws + ly.lc);
+  int32_t* rid = reinterpret_cast<int32_t*>(ws + ly.ids);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int w0 = params->window_left;
+
+  // the three calls are plain RoPE attention (no period) on two id arrays
+  prope_params call = *params;
+  call.mode = PROPE_ROPE;
+  call.remap_scale = 1;
+  call.period = 0;
+  if (launch_remap_ids(pos, rid, int64_t(B) * S, make_fastdiv(static_cast<uint32_t>(params->remap_scale)), st) !=
+      hipSuccess)
+    return PROPE_ERR_HIP;
+  // B: full causal attention at the remote ids, written straight into o
+  call.window_left = -1;
+  int rc = run_prefill(prefill_args(q, k, v, o, lb, rid, B, S, Hq, Hkv, d, call), dt, stream);
+  if (rc != PROPE_OK) return rc;
+  const bool windows = w0 >= 0;  // w0 = -1: no local window, the result is B alone
+  if (windows) {
+    // A: the local window at the ids themselves; C: the local window at the remote ids
+    call.window_left = w0;
+    rc = run_prefill(prefill_args(q, k, v, oa, la, pos, B, S, Hq, Hkv, d, call), dt, stream);
+    if (rc != PROPE_OK) return rc;
+    rc = run_prefill(prefill_args(q, k, v, oc, lc, rid, B, S, Hq, Hkv, d, call), dt, stream);
+    if (rc != PROPE_OK) return rc;
+  }
+  return launch_eq7_merge(oa, la, o, lb, oc, lc, lse, B, S, Hq, d, dt, windows, st) == hipSuccess ? PROPE_OK
+                                                                                               : PROPE_ERR_HIP;
 }
 
 size_t prope_decode_workspace_size(int B, int Lmax, int Hq, int d) {

@@ -60,5 +60,9 @@ hipError_t launch_rope_apply(const void* x, void* y, const int32_t* pos, int B, 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_fp32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_remap_ids(const int32_t* pos, int32_t* out, int64_t n, const FastDiv& s, hipStream_t stream);
+hipError_t launch_eq7_merge(const void* oa, const float* la, void* o, const float* lb, const void* oc,
+                            const float* lc, float* lse, int B, int S, int Hq, int d, int dt, bool windows,
+                            hipStream_t stream);
 
 }  // namespace prope

@@ -46,11 +46,15 @@ def to_np(t) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def gpu_prefill(inputs, mode, **kw):
+def gpu_prefill(inputs, mode, unfused=False, **kw):
     dev = torch.device("cuda:0")
     q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
     pos = inputs["pos"].to(dev)
-    o, lse = P.prefill(q, k, v, pos if mode != "nope" else None, mode=mode, return_lse=True, **kw)
+    if unfused:
+        assert mode == "bifocal"
+        o, lse = P.prefill_bifocal_unfused(q, k, v, pos, return_lse=True, **kw)
+    else:
+        o, lse = P.prefill(q, k, v, pos if mode != "nope" else None, mode=mode, return_lse=True, **kw)
     torch.cuda.synchronize()
     return o, lse
 
@@ -64,9 +68,9 @@ def oracle_prefill(inputs, mode, dtype, rows=None, **kw):
     return O.prefill_ref(q, k, v, pos, mode, operand_round=dtype, rows=rows, **kw)
 
 
-def check_prefill(inputs, mode, dtype, rows=None, what="", **kw):
+def check_prefill(inputs, mode, dtype, rows=None, what="", unfused=False, **kw):
     t0 = time.time()
-    o, lse = gpu_prefill(inputs, mode, **kw)
+    o, lse = gpu_prefill(inputs, mode, unfused=unfused, **kw)
     t1 = time.time()
     o_ref, lse_ref = oracle_prefill(inputs, mode, dtype, rows=rows, **kw)
     t2 = time.time()

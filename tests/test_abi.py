@@ -109,6 +109,35 @@ def test_decode_rejects(kw, code):
     assert _decode(**kw) == code
 
 
+def _unfused(q=FAKE, k=FAKE, v=FAKE, o=FAKE, pos=FAKE, B=1, S=1000, Hq=4, Hkv=2, d=64, dt=0, params=None,
+             ws=FAKE, ws_bytes=None):
+    L = P.lib()
+    p = _params() if params is None else params
+    if ws_bytes is None:
+        ws_bytes = L.prope_bifocal_unfused_workspace_size(B, S, Hq, d, dt)
+    return L.prope_attn_prefill_bifocal_unfused(q, k, v, o, None, pos, B, S, Hq, Hkv, d, dt, ctypes.byref(p),
+                                                ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(params=_params(mode=P.ROPE, remap_scale=1)), INVALID), (dict(params=_params(mode=P.NOPE, remap_scale=1)), INVALID),
+    (dict(pos=None), INVALID), (dict(ws=None), INVALID), (dict(ws=FAKE + 16), INVALID),
+    (dict(ws_bytes=1000), WORKSPACE), (dict(d=96), INVALID), (dict(Hq=5, Hkv=2), INVALID),
+])
+def test_unfused_rejects(kw, code):
+    assert _unfused(**kw) == code
+
+
+def test_unfused_workspace_size_formula():
+    L = P.lib()
+    up = lambda x: (x + 255) // 256 * 256
+    for B, S, Hq, d, dt in [(1, 1000, 4, 64, 0), (2, 65536, 32, 128, 0), (1, 77, 3, 128, 1)]:
+        ob = up(B * S * Hq * d * (2 if dt == 0 else 4))
+        lb = up(B * Hq * S * 4)
+        assert L.prope_bifocal_unfused_workspace_size(B, S, Hq, d, dt) == 2 * ob + 3 * lb + up(B * S * 4)
+    assert L.prope_bifocal_unfused_workspace_size(0, 10, 4, 64, 0) == 0
+
+
 def test_workspace_size_formula():
     L = P.lib()
     # [B][Hq][ceil(Lmax / 2048)][d + 2] float32 partials

@@ -105,6 +105,42 @@ def test_prefill_period_equals_prereduced_ids():
     assert torch.equal(o1, o2)
 
 
+# ------------------------------------------------------------------ unfused bifocal (Jet-Long Eq. (7))
+
+UNFUSED = [c for c in SMALL if c[2] == "bifocal"] + [
+    ("unfused_w0_at_tile_edge", (1, 400, 8, 2, 128, "bf16"), "bifocal", dict(rope_base=1e6, remap_scale=2, window_left=63), None),
+    ("unfused_d64_gqa2", (2, 250, 4, 2, 64, "bf16"), "bifocal", dict(rope_base=1e4, remap_scale=3, window_left=40), None),
+]
+
+
+@pytest.mark.parametrize("name,shape,mode,kw,ids", UNFUSED, ids=[c[0] for c in UNFUSED])
+def test_unfused_bifocal_small(name, shape, mode, kw, ids):
+    """Three attention calls merged by Eq. (7) on the device == the direct oracle."""
+    B, S, Hq, Hkv, d, dtype = shape
+    inp = _inputs(B, S, Hq, Hkv, d, dtype, seed=zlib.crc32(name.encode()) % 1000, ids=ids)
+    check_prefill(inp, "bifocal", dtype, what=f"{name} unfused", unfused=True, **kw)
+
+
+def test_unfused_matches_fused():
+    inp = _inputs(1, 1000, 8, 2, 128, "bf16", seed=71)
+    kw = dict(rope_base=1e6, remap_scale=2, window_left=300)
+    from parity import gpu_prefill
+    o_f, l_f = gpu_prefill(inp, "bifocal", **kw)
+    o_u, l_u = gpu_prefill(inp, "bifocal", unfused=True, **kw)
+    assert_close(to_np(o_u), to_np(o_f), "bf16", "unfused vs fused")
+    assert float((l_u - l_f).abs().max()) < LSE_TOL["bf16"]
+
+
+def test_unfused_full_window_reduces_to_call_a():
+    """w0 >= S - 1: calls B and C see the same keys, W_B - W_C is exactly zero
+    and the merge returns call A (plain RoPE attention) unchanged."""
+    inp = _inputs(1, 300, 4, 2, 128, "bf16", seed=72)
+    from parity import gpu_prefill
+    o_u, _ = gpu_prefill(inp, "bifocal", unfused=True, rope_base=1e6, remap_scale=3, window_left=299)
+    o_r, _ = gpu_prefill(inp, "rope", rope_base=1e6, window_left=299)
+    assert torch.equal(o_u, o_r)
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def test_endprompt_fp32_full():
@@ -123,15 +159,15 @@ def test_prope_nope_8k_full(name):
     check_prefill(inp, w.mode, "bf16", what=w.name, **kw)
 
 
-@pytest.mark.parametrize("name", ["bifocal_64k", "bifocal_128k"])
-def test_bifocal_full_size_sampled_rows(name):
+@pytest.mark.parametrize("name,unfused", [("bifocal_64k", False), ("bifocal_128k", False), ("bifocal_64k", True)])
+def test_bifocal_full_size_sampled_rows(name, unfused):
     w = W.get(name)
     log(f"{name}: generating inputs")
     inp = W.make_prefill_inputs(w)
     rows = W.stratified_rows(w.S, w.window_left, n_uniform=48, seed=w.seed)
     log(f"{name}: {len(rows)} sampled rows")
-    check_prefill(inp, "bifocal", "bf16", rows=rows, what=w.name, rope_base=w.rope_base,
-                  remap_scale=w.remap_scale, window_left=w.window_left)
+    check_prefill(inp, "bifocal", "bf16", rows=rows, what=w.name + (" unfused" if unfused else ""),
+                  unfused=unfused, rope_base=w.rope_base, remap_scale=w.remap_scale, window_left=w.window_left)
 
 
 # ------------------------------------------------------------------ decode
