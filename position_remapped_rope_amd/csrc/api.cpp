@@ -250,7 +250,13 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_len = kv_len;
   a.ws = static_cast<float*>(workspace);
   a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv; a.D = d; a.G = Hq / Hkv;
-  a.n_chunks = (Lmax + kDecodeChunk - 1) / kDecodeChunk;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    n_cu = 256;
+  const int64_t wg_large = int64_t(B) * Hkv * ((Lmax + kDecodeChunkLarge - 1) / kDecodeChunkLarge);
+  a.chunk = wg_large <= n_cu ? kDecodeChunkLarge : kDecodeChunk;
+  a.n_chunks = (Lmax + a.chunk - 1) / a.chunk;
   a.mode = params->mode;
   a.window_left = params->window_left;
   a.scale_div = make_fastdiv(static_cast<uint32_t>(params->remap_scale));

@@ -9,7 +9,7 @@
 // written back. NOPE/ROPE caches already carry their rotation, so those modes
 // score q . k_j with an optional window.
 //
-// Kernel 1 (split): one workgroup per (chunk of kDecodeChunk keys, KV head,
+// Kernel 1 (split): one workgroup per (chunk of a.chunk keys, KV head,
 // sequence); each of its 4 waves streams a quarter of the chunk in steps of 32
 // keys with no workgroup barrier. Per step and wave:
 //   - K rows are loaded straight into the A-operand layout of
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const int kl = lane & 15, kg = lane >> 4;
   const int G = a.G;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);  // a length outside [0, Lmax] never reads past the cache
-  const int jbeg = chunk * kDecodeChunk;
+  const int jbeg = chunk * a.chunk;
   const size_t head_stride = size_t(a.n_chunks) * (D + 2);
   float* wsb = a.ws + (size_t(b) * a.Hq + size_t(kvh) * G) * head_stride + size_t(chunk) * (D + 2);
 
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
     }
     return;
   }
-  const int jend = min(L, jbeg + kDecodeChunk);
+  const int jend = min(L, jbeg + a.chunk);
   const int pq = L - 1;
   const float sl2 = a.scale_log2;
   const int w0 = a.window_left;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const bool affine = (16 % sdiv) == 0;
   uint32_t ph[KSTEPS][4], inc[KSTEPS][4];
   // this wave's keys
-  const int per_wave = kDecodeChunk / WAVES;
+  const int per_wave = a.chunk / WAVES;
   const int wbeg = jbeg + wave * per_wave;
   const int wend = min(jend, wbeg + per_wave);
   if (MODE == kBifocal) {
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a)
   __shared__ float4 ored[CG][DV];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
-  const int nc = (L + kDecodeChunk - 1) / kDecodeChunk;
+  const int nc = (L + a.chunk - 1) / a.chunk;
   const size_t stride = D + 2;
   const float* wsb = a.ws + (size_t(b) * a.Hq + h) * size_t(a.n_chunks) * stride;
 

@@ -42,6 +42,7 @@ struct DecodeArgs {
   const int32_t* kv_len;
   float* ws;  // [B][Hq][n_chunks][D + 2]
   int B, Lmax, Hq, Hkv, D, G;
+  int chunk;  // keys per workgroup (a multiple of 4 * 32)
   int n_chunks;
   int mode;
   int window_left;
@@ -50,7 +51,12 @@ struct DecodeArgs {
   RopeFreq f;
 };
 
-constexpr int kDecodeChunk = 2048;  // keys per split-K chunk (512 per wave)
+// Keys per split-K workgroup: 2048 (512 per wave), or 4096 when that grid
+// still has at most one workgroup per compute unit (a single balanced round
+// with longer streams per wave measured faster there). The workspace is sized
+// for the smaller chunk.
+constexpr int kDecodeChunk = 2048;
+constexpr int kDecodeChunkLarge = 4096;
 
 // Fill F_i = round(theta_i / (2 pi) * 2^64), theta_i = base^(-2i/d), in long double.
 void fill_rope_freq(RopeFreq& f, int d, double base);
