@@ -75,7 +75,11 @@ typedef struct {
                             BIFOCAL: w0 >= -1, routing only; -1 = every key remote        */
   double rope_base;      /* Theta > 1 (e.g. 1e4, 1e6); ignored by NOPE                    */
   float softmax_scale;   /* > 0, or 0 for 1/sqrt(d)                                      */
-  int32_t reserved;      /* must be 0                                                    */
+  int32_t w_pretrained;  /* 0: the remote scale is remap_scale. > 0 (BIFOCAL only, with
+                            remap_scale = 1): the dynamic group size of Jet-Long section
+                            3.1, Eq. (2), s = G(L) = max(1, ceil(L / w_pretrained)), with L
+                            the sequence length (prefill: S; decode: kv_len[b], per
+                            sequence, so a batch may straddle a boundary)              */
 } prope_params;
 
 /*

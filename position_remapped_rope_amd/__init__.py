@@ -38,7 +38,7 @@ class PropeParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("period", ctypes.c_int32),
                 ("remap_scale", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("w_pretrained", ctypes.c_int32)]
 
 
 _lib = None
@@ -88,10 +88,10 @@ def _check(code: int):
         raise PropeError(status_string(code))
 
 
-def _params(mode, rope_base, period, remap_scale, window_left, softmax_scale) -> PropeParams:
+def _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained=0) -> PropeParams:
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
     return PropeParams(m, int(period), int(remap_scale), int(window_left), float(rope_base),
-                       float(softmax_scale), 0)
+                       float(softmax_scale), int(w_pretrained))
 
 
 def _dtype_code(t) -> int:
@@ -146,7 +146,7 @@ def rope_apply(x, pos, rope_base: float, out=None):
 
 def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
             remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
-            out=None, lse=None, return_lse: bool = False):
+            out=None, lse=None, return_lse: bool = False, w_pretrained: int = 0):
     """Causal attention with RoPE fused under remapped ids (see include/prope.h).
 
     q [B,S,Hq,d], k/v [B,S,Hkv,d] unrotated; pos int32 [B,S] (None for NoPE).
@@ -165,7 +165,7 @@ def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale)
+    p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained)
     _check(L.prope_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos),
                                 B, S, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p), _stream(q)))
     return (o, lse) if return_lse else o
@@ -177,7 +177,7 @@ def bifocal_unfused_workspace_size(B: int, S: int, Hq: int, d: int, dtype_code: 
 
 def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: int = 1, window_left: int = -1,
                             softmax_scale: float = 0.0, out=None, lse=None, workspace=None,
-                            return_lse: bool = False):
+                            return_lse: bool = False, w_pretrained: int = 0):
     """Bifocal prefill as three attention calls merged by Jet-Long Eq. (7) (see include/prope.h)."""
     import torch
     L = lib()
@@ -195,7 +195,7 @@ def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: i
     need = L.prope_bifocal_unfused_workspace_size(B, S, Hq, d, _dtype_code(q))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    p = _params("bifocal", rope_base, 0, remap_scale, window_left, softmax_scale)
+    p = _params("bifocal", rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained)
     _check(L.prope_attn_prefill_bifocal_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos),
                                                 B, S, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p),
                                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -205,7 +205,7 @@ def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: i
 
 def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
            remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
-           out=None, lse=None, workspace=None, return_lse: bool = False):
+           out=None, lse=None, workspace=None, return_lse: bool = False, w_pretrained: int = 0):
     """One decode step: q [B,Hq,d] base-rotated, caches [B,Lmax,Hkv,d], kv_len int32 [B]."""
     import torch
     L = lib()
@@ -224,7 +224,7 @@ def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
     need = L.prope_decode_workspace_size(B, Lmax, Hq, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    p = _params(mode, rope_base, 0, remap_scale, window_left, softmax_scale)
+    p = _params(mode, rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained)
     _check(L.prope_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
                                _ptr(kv_len), B, Lmax, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -37,7 +37,8 @@ bool valid_base(double b) { return isfinite(b) && b > 1.0; }
 // cache already carries the layer's rotation).
 int check_params(const prope_params* p, bool decode) {
   if (!p) return PROPE_ERR_INVALID_ARG;
-  if (p->reserved != 0) return PROPE_ERR_INVALID_ARG;
+  if (p->w_pretrained < 0) return PROPE_ERR_INVALID_ARG;
+  if (p->w_pretrained > 0 && (p->mode != PROPE_BIFOCAL || p->remap_scale != 1)) return PROPE_ERR_INVALID_ARG;
   if (p->mode != PROPE_NOPE && p->mode != PROPE_ROPE && p->mode != PROPE_BIFOCAL)
     return PROPE_ERR_INVALID_ARG;
   if (p->period < 0 || p->remap_scale < 1 || p->window_left < -1) return PROPE_ERR_INVALID_ARG;
@@ -46,6 +47,14 @@ int check_params(const prope_params* p, bool decode) {
   if (p->remap_scale != 1 && p->mode != PROPE_BIFOCAL) return PROPE_ERR_INVALID_ARG;
   if (p->mode != PROPE_NOPE && !valid_base(p->rope_base)) return PROPE_ERR_INVALID_ARG;
   return PROPE_OK;
+}
+
+// The remote scale s for a sequence of length L: remap_scale, or the dynamic
+// group size of Jet-Long Eq. (2) when w_pretrained > 0.
+int remote_scale(const prope_params& p, int64_t L) {
+  if (p.w_pretrained <= 0) return p.remap_scale;
+  const int64_t g = (L + p.w_pretrained - 1) / p.w_pretrained;
+  return g < 1 ? 1 : static_cast<int>(g);
 }
 
 float scale_log2(const prope_params* p, int d) {
@@ -84,7 +93,7 @@ PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, f
   a.period = p.period;
   a.window_left = p.window_left;
   a.period_div = make_fastdiv(p.period > 0 ? static_cast<uint32_t>(p.period) : 1u);
-  a.scale_div = make_fastdiv(static_cast<uint32_t>(p.remap_scale));
+  a.scale_div = make_fastdiv(static_cast<uint32_t>(remote_scale(p, S)));
   a.scale_log2 = scale_log2(&p, d);
   fill_rope_freq(a.f, d, p.mode == PROPE_NOPE ? 10000.0 : p.rope_base);
   return a;
@@ -200,8 +209,9 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
   call.mode = PROPE_ROPE;
   call.remap_scale = 1;
   call.period = 0;
-  if (launch_remap_ids(pos, rid, int64_t(B) * S, make_fastdiv(static_cast<uint32_t>(params->remap_scale)), st) !=
-      hipSuccess)
+  call.w_pretrained = 0;
+  if (launch_remap_ids(pos, rid, int64_t(B) * S, make_fastdiv(static_cast<uint32_t>(remote_scale(*params, S))),
+                       st) != hipSuccess)
     return PROPE_ERR_HIP;
   // B: full causal attention at the remote ids, written straight into o
   call.window_left = -1;
@@ -260,6 +270,7 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
   a.mode = params->mode;
   a.window_left = params->window_left;
   a.scale_div = make_fastdiv(static_cast<uint32_t>(params->remap_scale));
+  a.w_pre = params->w_pretrained;
   a.scale_log2 = scale_log2(params, d);
   fill_rope_freq(a.f, d, params->mode == PROPE_NOPE ? 10000.0 : params->rope_base);
   const hipError_t e = launch_decode_bf16(a, static_cast<hipStream_t>(stream));

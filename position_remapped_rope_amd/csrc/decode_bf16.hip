@@ -112,7 +112,10 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   // in the local view (as given) and the remote view RoPE(q, dq), both bf16.
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(kvh) * G) * D;
   u32x4_t qloc[KSTEPS], qrem[KSTEPS];
-  const int dq = MODE == kBifocal ? static_cast<int>(fastdiv(static_cast<uint32_t>(pq), a.scale_div)) - pq : 0;
+  // remote scale: fixed, or Jet-Long Eq. (2)'s group size for this sequence's length
+  const FastDiv sdv = a.w_pre > 0 ? make_fastdiv(static_cast<uint32_t>(max(1, (L + a.w_pre - 1) / a.w_pre)))
+                                  : a.scale_div;
+  const int dq = MODE == kBifocal ? static_cast<int>(fastdiv(static_cast<uint32_t>(pq), sdv)) - pq : 0;
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4_t w = {0, 0, 0, 0};
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   // carries dropped from the low 32 bits cost at most 2^-32 turn per step.
   // Otherwise every phase is formed exactly from the frequency table in LDS.
   __shared__ uint2 ftab[D / 2];
-  const int sdiv = static_cast<int>(a.scale_div.div);
+  const int sdiv = static_cast<int>(sdv.div);
   const bool affine = (16 % sdiv) == 0;
   uint32_t ph[KSTEPS][4], inc[KSTEPS][4];
   // this wave's keys
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   if (MODE == kBifocal) {
     if (tid < D / 2) ftab[tid] = make_uint2(a.f.lo[tid], a.f.hi[tid]);
     const int j = wbeg + kl;
-    const int dk0 = static_cast<int>(fastdiv(static_cast<uint32_t>(j), a.scale_div)) - j;
+    const int dk0 = static_cast<int>(fastdiv(static_cast<uint32_t>(j), sdv)) - j;
     const int d16 = affine ? 16 / sdiv - 16 : 0;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
       }
       if (any_remote) {
         const int j = jb + kl;  // this lane's key
-        const int dk = affine ? 0 : static_cast<int>(fastdiv(static_cast<uint32_t>(j), a.scale_div)) - j;
+        const int dk = affine ? 0 : static_cast<int>(fastdiv(static_cast<uint32_t>(j), sdv)) - j;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           u32x4_t y;

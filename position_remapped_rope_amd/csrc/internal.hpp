@@ -46,7 +46,8 @@ struct DecodeArgs {
   int n_chunks;
   int mode;
   int window_left;
-  FastDiv scale_div;
+  FastDiv scale_div;  // remote scale s (w_pre == 0)
+  int w_pre;          // > 0: s = max(1, ceil(kv_len / w_pre)) per sequence
   float scale_log2;
   RopeFreq f;
 };

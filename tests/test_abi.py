@@ -52,10 +52,10 @@ def test_group_size_golden():
 
 
 def _params(**kw):
-    d = dict(mode=P.BIFOCAL, period=0, remap_scale=2, window_left=8, rope_base=1e6, softmax_scale=0.0, reserved=0)
+    d = dict(mode=P.BIFOCAL, period=0, remap_scale=2, window_left=8, rope_base=1e6, softmax_scale=0.0, w_pretrained=0)
     d.update(kw)
     return P.PropeParams(d["mode"], d["period"], d["remap_scale"], d["window_left"], d["rope_base"],
-                         d["softmax_scale"], d["reserved"])
+                         d["softmax_scale"], d["w_pretrained"])
 
 
 def _prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos=FAKE, B=1, S=16, Hq=4, Hkv=2, d=128, dt=0,
@@ -76,7 +76,9 @@ def _prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos=FAKE, B=1, S=16, Hq=4
     dict(params=_params(mode=P.ROPE, remap_scale=2)),     # remap_scale only with BIFOCAL
     dict(params=_params(window_left=-2)), dict(params=_params(mode=5)),
     dict(params=_params(rope_base=1.0)), dict(params=_params(rope_base=float("nan"))),
-    dict(params=_params(softmax_scale=-1.0)), dict(params=_params(reserved=1)),
+    dict(params=_params(softmax_scale=-1.0)), dict(params=_params(w_pretrained=-1)),
+    dict(params=_params(w_pretrained=64)),                              # dynamic G needs remap_scale 1
+    dict(params=_params(mode=P.ROPE, remap_scale=1, w_pretrained=64)),  # dynamic G is bifocal only
     dict(byref=False),
 ])
 def test_prefill_rejects(kw):

@@ -223,6 +223,80 @@ def test_decode_workspace_reuse():
     assert_close(to_np(o_reuse), o_ref, "bf16", "reused workspace vs oracle")
 
 
+# ------------------------------------------------------------------ dynamic group size (Jet-Long Eq. (2))
+
+def test_dynamic_g_prefill_equals_fixed_scale():
+    """w_pretrained > 0 uses s = G(S); with G(S) = 3 the result is the fixed-s call's, bit for bit."""
+    inp = _inputs(1, 700, 4, 2, 128, "bf16", seed=81)
+    from parity import gpu_prefill
+    kw = dict(rope_base=1e6, window_left=100)
+    o_dyn, _ = gpu_prefill(inp, "bifocal", w_pretrained=256, **kw)  # ceil(700 / 256) = 3
+    o_fix, _ = gpu_prefill(inp, "bifocal", remap_scale=3, **kw)
+    assert torch.equal(o_dyn, o_fix)
+    o_un, _ = gpu_prefill(inp, "bifocal", unfused=True, w_pretrained=256, **kw)
+    o_unf, _ = gpu_prefill(inp, "bifocal", unfused=True, remap_scale=3, **kw)
+    assert torch.equal(o_un, o_unf)
+
+
+def test_dynamic_g_decode_batch_straddles_boundaries():
+    """One decode call whose sequences sit on both sides of w_pretrained multiples:
+    each uses its own s = G(kv_len)."""
+    B, L, Hq, Hkv, d = 4, 1600, 8, 2, 128
+    w = W.Workload("t", "decode", B=B, S=L, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", mode="bifocal", rope_base=1e6, seed=82)
+    inp = W.make_decode_inputs(w)
+    lens = [512, 513, 1025, 1600]
+    inp["kv_len"] = torch.tensor(lens, dtype=torch.int32)
+    kw = dict(rope_base=1e6, window_left=200)
+    o, lse = gpu_decode(inp, mode="bifocal", w_pretrained=512, **kw)
+    for b, n in enumerate(lens):
+        G = O.group_size(n, 512)
+        sub = {"q": inp["q"][b:b + 1], "k_cache": inp["k_cache"][b:b + 1], "v_cache": inp["v_cache"][b:b + 1],
+               "kv_len": inp["kv_len"][b:b + 1]}
+        o_ref, lse_ref = oracle_decode(sub, "bifocal", remap_scale=G, **kw)
+        assert_close(to_np(o[b:b + 1]), o_ref, "bf16", f"len {n} G {G}")
+        assert float(np.max(np.abs(lse.cpu().numpy()[b] - lse_ref[0]))) < LSE_TOL["bf16"]
+
+
+def test_generation_across_group_size_boundaries():
+    """Prefill a prompt, then generate token by token across L = w_pre and 2 w_pre:
+    each new key is rotated at its own position into the cache (Jet-Long Eq. (4)),
+    the cache is never rewritten, and the decode at length L (s = G(L) from the
+    kernel) equals the last row of the direct bifocal oracle over the first L tokens."""
+    w_pre, S0, steps = 256, 240, 290
+    Hq, Hkv, d = 4, 2, 128
+    kw = dict(rope_base=1e6, window_left=100)
+    n = S0 + steps
+    inp = _inputs(1, n, Hq, Hkv, d, "bf16", seed=83)
+    dev = torch.device("cuda:0")
+    q_all, k_all, v_all, pos_all = (inp[x].to(dev) for x in ("q", "k", "v", "pos"))
+    # prompt: bifocal prefill at G(S0) = 1, and the base-rotated cache
+    o_pre = P.prefill(q_all[:, :S0].contiguous(), k_all[:, :S0].contiguous(), v_all[:, :S0].contiguous(),
+                      pos_all[:, :S0].contiguous(), mode="bifocal", w_pretrained=w_pre, **kw)
+    kc = torch.zeros((1, n, Hkv, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    P.rope_apply(k_all[:, :S0].contiguous(), pos_all[:, :S0].contiguous(), kw["rope_base"], out=kc[:, :S0])
+    vc[:, :S0] = v_all[:, :S0]
+    outs = {}
+    for L in range(S0 + 1, n + 1):
+        p = pos_all[:, L - 1:L].contiguous()
+        P.rope_apply(k_all[:, L - 1:L].contiguous(), p, kw["rope_base"], out=kc[:, L - 1:L])
+        vc[:, L - 1] = v_all[:, L - 1]
+        ql = P.rope_apply(q_all[:, L - 1:L].contiguous(), p, kw["rope_base"])[:, 0].contiguous()
+        o = P.decode(ql, kc, vc, torch.tensor([L], dtype=torch.int32, device=dev), mode="bifocal",
+                     w_pretrained=w_pre, **kw)
+        outs[L] = o
+    torch.cuda.synchronize()
+    qn, kn, vn, pn = (to_np(inp[x]) if x != "pos" else inp[x].numpy() for x in ("q", "k", "v", "pos"))
+    ref0, _ = O.prefill_ref(qn[:, :S0], kn[:, :S0], vn[:, :S0], pn[:, :S0], "bifocal", remap_scale=1,
+                            operand_round="bf16", **kw)
+    assert_close(to_np(o_pre), ref0, "bf16", "prompt prefill at G = 1")
+    for L in (S0 + 1, w_pre, w_pre + 1, 2 * w_pre, 2 * w_pre + 1, n):
+        G = O.group_size(L, w_pre)
+        ref, _ = O.prefill_ref(qn[:, :L], kn[:, :L], vn[:, :L], pn[:, :L], "bifocal", remap_scale=G,
+                               rows=[L - 1], **kw)
+        assert_close(to_np(outs[L]), ref[:, 0], "bf16", f"decode at L = {L} (G = {G})")
+
+
 def test_decode_matches_prefill_last_row():
     """Cache built with rope_apply (Jet-Long Eq. (4)) + decode == last prefill row."""
     B, S, Hq, Hkv, d = 1, 1100, 8, 2, 128
