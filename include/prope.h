@@ -65,6 +65,12 @@ typedef enum {
                         remote view at ids floor(p / remap_scale)                   */
 } prope_mode;
 
+typedef enum {
+  PROPE_REMOTE_ALIAS = 0,  /* remote ids floor(p / s) (Jet-Long Eq. (3))                   */
+  PROPE_REMOTE_INTERP = 1  /* remote angle p * theta_i / s: the frequency-interpolation
+                              mapping of Jet-Long section 4.5 (Table 6), unfloored        */
+} prope_remote_map;
+
 typedef struct {
   int32_t mode;          /* prope_mode                                                   */
   int32_t period;        /* P >= 0; 0 = no period. ROPE mode only (else must be 0)       */
@@ -80,6 +86,9 @@ typedef struct {
                             3.1, Eq. (2), s = G(L) = max(1, ceil(L / w_pretrained)), with L
                             the sequence length (prefill: S; decode: kv_len[b], per
                             sequence, so a batch may straddle a boundary)              */
+  int32_t remote_map;    /* prope_remote_map; PROPE_REMOTE_INTERP is BIFOCAL only, and
+                            not with w_pretrained > 0 in decode or with the unfused call
+                            (PROPE_ERR_UNSUPPORTED)                                     */
 } prope_params;
 
 /*

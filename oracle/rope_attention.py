@@ -99,6 +99,22 @@ def remote_index(p, G: int):
     return np.floor_divide(np.asarray(p, dtype=np.int64), int(G))
 
 
+def remote_position(p, G: int, remote_map: str = "alias"):
+    """The remote view's rotation position of position p.
+
+    "alias": floor(p / G), the default mapping (Jet-Long page, Eq. (3));
+    "interp": p / G unfloored, i.e. every frequency theta_i divided by G at the
+    original positions: the frequency-interpolation mapping the same page
+    compares against aliasing in section 4.5 (Table 6), taken in its plainest
+    (uniform, linear) form.
+    """
+    if remote_map == "alias":
+        return remote_index(p, G)
+    if remote_map == "interp":
+        return np.asarray(p, dtype=np.float64) / float(G)
+    raise ValueError(remote_map)
+
+
 def rope_apply_ref(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     """y = R_pos x per token: x [B,S,H,d], pos int [B,S] (negative ids allowed)."""
     return rotate(x, np.asarray(pos, dtype=np.int64)[:, :, None], base)
@@ -152,18 +168,20 @@ def _softmax_rows(scores: np.ndarray, keep: np.ndarray, vals: np.ndarray):
     return o, lse
 
 
-def _check_mode(mode, period, remap_scale, window_left):
+def _check_mode(mode, period, remap_scale, window_left, remote_map="alias"):
     if mode not in MODES:
         raise ValueError(f"mode must be one of {MODES}")
     if period < 0 or remap_scale < 1 or window_left < -1:
         raise ValueError("bad period / remap_scale / window_left")
+    if remote_map not in ("alias", "interp") or (remote_map == "interp" and mode != "bifocal"):
+        raise ValueError("bad remote_map")
 
 
 def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0,
                 remap_scale: int = 1, window_left: int = -1,
                 softmax_scale: Optional[float] = None, operand_round: Optional[str] = None,
-                rows: Optional[np.ndarray] = None, max_block_elems: int = 1 << 24
-                ) -> Tuple[np.ndarray, np.ndarray]:
+                rows: Optional[np.ndarray] = None, max_block_elems: int = 1 << 24,
+                remote_map: str = "alias") -> Tuple[np.ndarray, np.ndarray]:
     """Causal attention with RoPE under remapped ids, computed directly.
 
     q [B,S,Hq,d], k/v [B,S,Hkv,d] (unrotated), pos int [B,S]. The KV head of
@@ -176,11 +194,12 @@ def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0
                                                          (P-RoPE page, Eq. (3)-(5))
       bifocal: i - j <= w0: (R_{p_i} q_i) . (R_{p_j} k_j)
                i - j >  w0: (R_{f(p_i)} q_i) . (R_{f(p_j)} k_j), f(x) = floor(x/s)
-                                                         (Jet-Long page, Eq. (1), (3))
+                                                         (Jet-Long page, Eq. (1), (3)),
+                            or f(x) = x / s with remote_map="interp" (section 4.5)
     then scaled by softmax_scale (default 1/sqrt(d)). In nope/rope modes a
     window_left >= 0 also drops keys with i - j > window_left.
     """
-    _check_mode(mode, period, remap_scale, window_left)
+    _check_mode(mode, period, remap_scale, window_left, remote_map)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -207,8 +226,8 @@ def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0
             r = periodic_index(p, period)
             kb = round_operand(rotate(k[b], r[:, None], rope_base), operand_round)
             qb = round_operand(rotate(q[b][rows], r[rows][:, None], rope_base), operand_round)
-        else:  # bifocal: base rotation at p, remote rotation at floor(p / s)
-            rr = remote_index(p, remap_scale)
+        else:  # bifocal: base rotation at p, remote rotation at f(p)
+            rr = remote_position(p, remap_scale, remote_map)
             kb = round_operand(rotate(k[b], p[:, None], rope_base), operand_round)
             qb = round_operand(rotate(q[b][rows], p[rows][:, None], rope_base), operand_round)
             kr = round_operand(rotate(k[b], rr[:, None], rope_base), operand_round)
@@ -238,8 +257,8 @@ def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0
 
 def decode_ref(q, k_cache, v_cache, kv_len, mode: str = "bifocal", rope_base: float = 1e6,
                remap_scale: int = 1, window_left: int = -1,
-               softmax_scale: Optional[float] = None, operand_round: Optional[str] = None
-               ) -> Tuple[np.ndarray, np.ndarray]:
+               softmax_scale: Optional[float] = None, operand_round: Optional[str] = None,
+               remote_map: str = "alias") -> Tuple[np.ndarray, np.ndarray]:
     """One decode step against a cache of base-rotated keys.
 
     q [B,Hq,d] is the query already rotated at its own position p_q = kv_len-1;
@@ -248,12 +267,14 @@ def decode_ref(q, k_cache, v_cache, kv_len, mode: str = "bifocal", rope_base: fl
 
     bifocal: local keys (p_q - j <= w0) score q . k_j; remote keys score
     RoPE(q, dq) . RoPE(k_j, dk_j) with dq = floor(p_q/s) - p_q and
-    dk_j = floor(j/s) - j (Jet-Long page, Eq. (5)-(6)).
+    dk_j = floor(j/s) - j (Jet-Long page, Eq. (5)-(6)); with remote_map="interp"
+    the remote positions are p_q / s and j / s, so dq = p_q/s - p_q and
+    dk_j = j/s - j.
     nope/rope: the cache and q already carry whatever rotation the layer uses,
     so scores are q . k_j, with keys p_q - j > window_left dropped if
     window_left >= 0.
     """
-    _check_mode(mode, 0, remap_scale, window_left)
+    _check_mode(mode, 0, remap_scale, window_left, remote_map)
     q = np.asarray(q, dtype=np.float64)
     kc = np.asarray(k_cache, dtype=np.float64)
     vc = np.asarray(v_cache, dtype=np.float64)
@@ -273,8 +294,8 @@ def decode_ref(q, k_cache, v_cache, kv_len, mode: str = "bifocal", rope_base: fl
         if mode != "bifocal" and window_left >= 0:
             keep = dist <= window_left
         if mode == "bifocal":
-            dq = int(remote_index(pq, remap_scale)) - pq                 # Eq. (5)
-            dk = remote_index(j, remap_scale) - j
+            dq = remote_position(pq, remap_scale, remote_map) - pq       # Eq. (5)
+            dk = remote_position(j, remap_scale, remote_map) - j
             k_rem = round_operand(rotate(kc[b, :L], dk[:, None], rope_base), operand_round)
             q_rem = round_operand(rotate(q[b], dq, rope_base), operand_round)
         for h in range(Hq):
@@ -345,7 +366,7 @@ def bifocal_eq7_ref(q, k, v, pos, rope_base: float, remap_scale: int, window_lef
 
 def brute_force_prefill(q, k, v, pos, mode: str, rope_base: float, period: int = 0,
                         remap_scale: int = 1, window_left: int = -1,
-                        softmax_scale: Optional[float] = None):
+                        softmax_scale: Optional[float] = None, remote_map: str = "alias"):
     """Pure-Python loops over (b, h, i, j, pair) with explicit 2x2 rotation blocks.
 
     For tiny inputs only. Returns O as nested float lists shaped [B][S][Hq][d].
@@ -393,8 +414,10 @@ def brute_force_prefill(q, k, v, pos, mode: str, rope_base: float, period: int =
                     else:
                         if dist <= window_left:
                             ri, rj = pos[b][i], pos[b][j]
-                        else:
+                        elif remote_map == "alias":
                             ri, rj = pos[b][i] // remap_scale, pos[b][j] // remap_scale
+                        else:
+                            ri, rj = pos[b][i] / remap_scale, pos[b][j] / remap_scale
                         s_ij = dot(block_rotate(q[b][i][h], ri), block_rotate(k[b][j][g], rj))
                     scores.append(s_ij * scale)
                     idx.append(j)

@@ -17,6 +17,8 @@ __all__ = ["NOPE", "ROPE", "BIFOCAL", "PropeError", "lib", "lib_path", "rope_app
 
 NOPE, ROPE, BIFOCAL = 0, 1, 2
 _MODES = {"nope": NOPE, "rope": ROPE, "bifocal": BIFOCAL}
+REMOTE_ALIAS, REMOTE_INTERP = 0, 1
+_REMOTE = {"alias": REMOTE_ALIAS, "interp": REMOTE_INTERP}
 BF16, FP32 = 0, 1
 
 EXPORTED_SYMBOLS = ("prope_attn_prefill", "prope_attn_prefill_bifocal_unfused",
@@ -38,7 +40,7 @@ class PropeParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("period", ctypes.c_int32),
                 ("remap_scale", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("w_pretrained", ctypes.c_int32)]
+                ("w_pretrained", ctypes.c_int32), ("remote_map", ctypes.c_int32)]
 
 
 _lib = None
@@ -88,10 +90,12 @@ def _check(code: int):
         raise PropeError(status_string(code))
 
 
-def _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained=0) -> PropeParams:
+def _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained=0,
+            remote_map="alias") -> PropeParams:
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    r = _REMOTE[remote_map] if isinstance(remote_map, str) else int(remote_map)
     return PropeParams(m, int(period), int(remap_scale), int(window_left), float(rope_base),
-                       float(softmax_scale), int(w_pretrained))
+                       float(softmax_scale), int(w_pretrained), r)
 
 
 def _dtype_code(t) -> int:
@@ -146,7 +150,7 @@ def rope_apply(x, pos, rope_base: float, out=None):
 
 def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
             remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
-            out=None, lse=None, return_lse: bool = False, w_pretrained: int = 0):
+            out=None, lse=None, return_lse: bool = False, w_pretrained: int = 0, remote_map="alias"):
     """Causal attention with RoPE fused under remapped ids (see include/prope.h).
 
     q [B,S,Hq,d], k/v [B,S,Hkv,d] unrotated; pos int32 [B,S] (None for NoPE).
@@ -165,7 +169,7 @@ def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained)
+    p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained, remote_map)
     _check(L.prope_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos),
                                 B, S, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p), _stream(q)))
     return (o, lse) if return_lse else o
@@ -205,7 +209,8 @@ def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: i
 
 def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
            remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
-           out=None, lse=None, workspace=None, return_lse: bool = False, w_pretrained: int = 0):
+           out=None, lse=None, workspace=None, return_lse: bool = False, w_pretrained: int = 0,
+           remote_map="alias"):
     """One decode step: q [B,Hq,d] base-rotated, caches [B,Lmax,Hkv,d], kv_len int32 [B]."""
     import torch
     L = lib()
@@ -224,7 +229,7 @@ def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
     need = L.prope_decode_workspace_size(B, Lmax, Hq, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    p = _params(mode, rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained)
+    p = _params(mode, rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained, remote_map)
     _check(L.prope_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
                                _ptr(kv_len), B, Lmax, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -10,14 +10,15 @@
 
 namespace prope {
 
-void fill_rope_freq(RopeFreq& f, int d, double base) {
-  // F_i = round(theta_i / (2 pi) * 2^64), theta_i = base^(-2i/d) (P-RoPE page, Eq. (1)).
+void fill_rope_freq(RopeFreq& f, int d, double base, int s) {
+  // F_i = round(theta_i / (2 pi s) * 2^64), theta_i = base^(-2i/d) (P-RoPE page, Eq. (1));
+  // s > 1 gives the interpolated frequencies theta_i / s.
   const long double two_pi = 2.0L * acosl(-1.0L);
   for (int i = 0; i < kMaxPairs; ++i) {
     uint64_t F = 0;
     if (i < d / 2) {
       const long double theta = powl(static_cast<long double>(base), -2.0L * i / d);
-      const long double turns = theta / two_pi * 18446744073709551616.0L;  // * 2^64
+      const long double turns = theta / (two_pi * s) * 18446744073709551616.0L;  // * 2^64
       F = static_cast<uint64_t>(turns + 0.5L);
     }
     f.lo[i] = static_cast<uint32_t>(F);
@@ -38,6 +39,8 @@ bool valid_base(double b) { return isfinite(b) && b > 1.0; }
 int check_params(const prope_params* p, bool decode) {
   if (!p) return PROPE_ERR_INVALID_ARG;
   if (p->w_pretrained < 0) return PROPE_ERR_INVALID_ARG;
+  if (p->remote_map != PROPE_REMOTE_ALIAS && p->remote_map != PROPE_REMOTE_INTERP) return PROPE_ERR_INVALID_ARG;
+  if (p->remote_map == PROPE_REMOTE_INTERP && p->mode != PROPE_BIFOCAL) return PROPE_ERR_INVALID_ARG;
   if (p->w_pretrained > 0 && (p->mode != PROPE_BIFOCAL || p->remap_scale != 1)) return PROPE_ERR_INVALID_ARG;
   if (p->mode != PROPE_NOPE && p->mode != PROPE_ROPE && p->mode != PROPE_BIFOCAL)
     return PROPE_ERR_INVALID_ARG;
@@ -93,9 +96,15 @@ PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, f
   a.period = p.period;
   a.window_left = p.window_left;
   a.period_div = make_fastdiv(p.period > 0 ? static_cast<uint32_t>(p.period) : 1u);
-  a.scale_div = make_fastdiv(static_cast<uint32_t>(remote_scale(p, S)));
+  const int s = remote_scale(p, S);
+  const bool interp = p.remote_map == PROPE_REMOTE_INTERP;
+  a.scale_div = make_fastdiv(static_cast<uint32_t>(interp ? 1 : s));
   a.scale_log2 = scale_log2(&p, d);
   fill_rope_freq(a.f, d, p.mode == PROPE_NOPE ? 10000.0 : p.rope_base);
+  if (interp)
+    fill_rope_freq(a.fr, d, p.rope_base, s);
+  else
+    a.fr = a.f;
   return a;
 }
 
@@ -191,6 +200,7 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
   const int pc = check_prefill(q, k, v, o, pos, B, S, Hq, Hkv, d, dt, params);
   if (pc != PROPE_OK) return pc;
   if (params->mode != PROPE_BIFOCAL || !pos || !workspace) return PROPE_ERR_INVALID_ARG;
+  if (params->remote_map != PROPE_REMOTE_ALIAS) return PROPE_ERR_UNSUPPORTED;  // the calls take integer ids
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return PROPE_ERR_INVALID_ARG;
   const UnfusedLayout ly = unfused_layout(B, S, Hq, d, dt);
   if (workspace_bytes < ly.total) return PROPE_ERR_WORKSPACE;
@@ -252,6 +262,8 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(o) |
        reinterpret_cast<uintptr_t>(workspace)) % 16)
     return PROPE_ERR_INVALID_ARG;
+  const bool interp = params->remote_map == PROPE_REMOTE_INTERP;
+  if (interp && params->w_pretrained > 0) return PROPE_ERR_UNSUPPORTED;  // per-sequence frequency tables
   if (workspace_bytes < prope_decode_workspace_size(B, Lmax, Hq, d)) return PROPE_ERR_WORKSPACE;
   // one sequence's cache slice is addressed with 32-bit byte offsets
   if (int64_t(Lmax) * Hkv * d * 2 >= (int64_t(1) << 32)) return PROPE_ERR_UNSUPPORTED;
@@ -269,10 +281,22 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
   a.n_chunks = (Lmax + a.chunk - 1) / a.chunk;
   a.mode = params->mode;
   a.window_left = params->window_left;
-  a.scale_div = make_fastdiv(static_cast<uint32_t>(params->remap_scale));
+  a.scale_div = make_fastdiv(static_cast<uint32_t>(interp ? 1 : params->remap_scale));
   a.w_pre = params->w_pretrained;
   a.scale_log2 = scale_log2(params, d);
   fill_rope_freq(a.f, d, params->mode == PROPE_NOPE ? 10000.0 : params->rope_base);
+  a.interp = interp;
+  if (interp) {  // correction frequencies theta_i / s - theta_i, modulo one turn
+    RopeFreq fs;
+    fill_rope_freq(fs, d, params->rope_base, params->remap_scale);
+    for (int i = 0; i < kMaxPairs; ++i) {
+      const uint64_t c = ((uint64_t(fs.hi[i]) << 32) | fs.lo[i]) - ((uint64_t(a.f.hi[i]) << 32) | a.f.lo[i]);
+      a.fr.lo[i] = static_cast<uint32_t>(c);
+      a.fr.hi[i] = static_cast<uint32_t>(c >> 32);
+    }
+  } else {
+    a.fr = a.f;
+  }
   const hipError_t e = launch_decode_bf16(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PROPE_OK : PROPE_ERR_HIP;
 }

@@ -4,9 +4,10 @@
 // (Eq. (4)) and is never rewritten. For a query at p_q = kv_len - 1, a key at
 // distance p_q - j <= w0 scores with the cached vectors as they are; a farther
 // key scores with the remote view RoPE(q, dq) . RoPE(k_j, dk_j), where
-// dq = floor(p_q/s) - p_q and dk_j = floor(j/s) - j (Eq. (5)-(6)). Both
-// corrections are formed in registers from exact integer phases; nothing is
-// written back. NOPE/ROPE caches already carry their rotation, so those modes
+// dq = floor(p_q/s) - p_q and dk_j = floor(j/s) - j (Eq. (5)-(6)); with the
+// frequency-interpolation mapping (same page, section 4.5) the corrections are
+// p_q * (theta_i/s - theta_i) and j * (theta_i/s - theta_i). Both are formed in
+// registers from exact integer phases; nothing is written back. NOPE/ROPE caches already carry their rotation, so those modes
 // score q . k_j with an optional window.
 //
 // Kernel 1 (split): one workgroup per (chunk of a.chunk keys, KV head,
@@ -115,7 +116,12 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   // remote scale: fixed, or Jet-Long Eq. (2)'s group size for this sequence's length
   const FastDiv sdv = a.w_pre > 0 ? make_fastdiv(static_cast<uint32_t>(max(1, (L + a.w_pre - 1) / a.w_pre)))
                                   : a.scale_div;
-  const int dq = MODE == kBifocal ? static_cast<int>(fastdiv(static_cast<uint32_t>(pq), sdv)) - pq : 0;
+  // correction index of position x: floor(x/s) - x (alias) or x itself (interpolation,
+  // whose correction frequencies theta_i / s - theta_i are in fr)
+  auto corr = [&](int x) __attribute__((always_inline)) {
+    return a.interp ? x : static_cast<int>(fastdiv(static_cast<uint32_t>(x), sdv)) - x;
+  };
+  const int dq = MODE == kBifocal ? corr(pq) : 0;
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4_t w = {0, 0, 0, 0};
@@ -127,7 +133,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
       for (int e = 0; e < 4; ++e) {
         const int pi = 4 * kg + 16 * ks + e;
         float sn, cs, y0, y1;
-        rope_sincos(dq, a.f.lo[pi], a.f.hi[pi], sn, cs);
+        rope_sincos(dq, a.fr.lo[pi], a.fr.hi[pi], sn, cs);
         rot_pair(bf16_lo(w[e]), bf16_hi(w[e]), cs, sn, y0, y1);
         y[e] = pack_bf16(y0, y1);
       }
@@ -143,24 +149,23 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   // Otherwise every phase is formed exactly from the frequency table in LDS.
   __shared__ uint2 ftab[D / 2];
   const int sdiv = static_cast<int>(sdv.div);
-  const bool affine = (16 % sdiv) == 0;
+  const bool affine = a.interp || (16 % sdiv) == 0;
   uint32_t ph[KSTEPS][4], inc[KSTEPS][4];
   // this wave's keys
   const int per_wave = a.chunk / WAVES;
   const int wbeg = jbeg + wave * per_wave;
   const int wend = min(jend, wbeg + per_wave);
   if (MODE == kBifocal) {
-    if (tid < D / 2) ftab[tid] = make_uint2(a.f.lo[tid], a.f.hi[tid]);
-    const int j = wbeg + kl;
-    const int dk0 = static_cast<int>(fastdiv(static_cast<uint32_t>(j), sdv)) - j;
-    const int d16 = affine ? 16 / sdiv - 16 : 0;
+    if (tid < D / 2) ftab[tid] = make_uint2(a.fr.lo[tid], a.fr.hi[tid]);
+    const int dk0 = corr(wbeg + kl);
+    const int d16 = a.interp ? 16 : affine ? 16 / sdiv - 16 : 0;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pi = 4 * kg + 16 * ks + e;
-        ph[ks][e] = phase_top(dk0, a.f.lo[pi], a.f.hi[pi]);
-        inc[ks][e] = phase_top(d16, a.f.lo[pi], a.f.hi[pi]);
+        ph[ks][e] = phase_top(dk0, a.fr.lo[pi], a.fr.hi[pi]);
+        inc[ks][e] = phase_top(d16, a.fr.lo[pi], a.fr.hi[pi]);
       }
     __syncthreads();
   }
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
       }
       if (any_remote) {
         const int j = jb + kl;  // this lane's key
-        const int dk = affine ? 0 : static_cast<int>(fastdiv(static_cast<uint32_t>(j), sdv)) - j;
+        const int dk = affine ? 0 : corr(j);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           u32x4_t y;

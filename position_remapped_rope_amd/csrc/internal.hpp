@@ -28,9 +28,10 @@ struct PrefillArgs {
   int period;       // ROPE: P (0 = none)
   int window_left;  // NOPE/ROPE: max kept i-j (-1 none); BIFOCAL: w0
   FastDiv period_div;
-  FastDiv scale_div;
-  float scale_log2;  // softmax scale * log2(e)
-  RopeFreq f;
+  FastDiv scale_div;  // remote ids floor(p / div): s (alias) or 1 (interpolation)
+  float scale_log2;   // softmax scale * log2(e)
+  RopeFreq f;         // theta_i at the base ids
+  RopeFreq fr;        // theta_i at the remote ids: theta_i (alias) or theta_i / s
 };
 
 struct DecodeArgs {
@@ -46,10 +47,13 @@ struct DecodeArgs {
   int n_chunks;
   int mode;
   int window_left;
-  FastDiv scale_div;  // remote scale s (w_pre == 0)
-  int w_pre;          // > 0: s = max(1, ceil(kv_len / w_pre)) per sequence
+  FastDiv scale_div;  // remote scale s (alias, w_pre == 0)
+  int w_pre;          // > 0: s = max(1, ceil(kv_len / w_pre)) per sequence (alias only)
+  int interp;         // remote angles p * theta_i / s instead of floor(p / s) * theta_i
   float scale_log2;
-  RopeFreq f;
+  RopeFreq f;         // theta_i
+  RopeFreq fr;        // correction frequencies: theta_i (alias, index floor(p/s) - p) or
+                      // theta_i / s - theta_i (interpolation, index p)
 };
 
 // Keys per split-K workgroup: 2048 (512 per wave), or 4096 when that grid
@@ -59,8 +63,8 @@ struct DecodeArgs {
 constexpr int kDecodeChunk = 2048;
 constexpr int kDecodeChunkLarge = 4096;
 
-// Fill F_i = round(theta_i / (2 pi) * 2^64), theta_i = base^(-2i/d), in long double.
-void fill_rope_freq(RopeFreq& f, int d, double base);
+// Fill F_i = round(theta_i / (2 pi s) * 2^64), theta_i = base^(-2i/d), in long double.
+void fill_rope_freq(RopeFreq& f, int d, double base, int s = 1);
 
 hipError_t launch_rope_apply(const void* x, void* y, const int32_t* pos, int B, int S, int H,
                              int d, int dt, const RopeFreq& f, hipStream_t stream);

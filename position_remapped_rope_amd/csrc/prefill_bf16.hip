@@ -5,7 +5,10 @@
 //   NOPE     q_i . k_j                                  (P-RoPE page, Eq. (6))
 //   ROPE     (R_r q_i) . (R_r k_j), r = p mod P or p    (P-RoPE page, Eq. (3)-(5))
 //   BIFOCAL  local  (i - j <= w0): RoPE at p
-//            remote (i - j >  w0): RoPE at floor(p / s) (Jet-Long page, Eq. (1), (3))
+//            remote (i - j >  w0): RoPE at floor(p / s) (Jet-Long page, Eq. (1), (3)),
+//            or with interpolated frequencies theta_i / s at p (same page,
+//            section 4.5): the remote pass reads ids floor(p / div) with the
+//            frequency table fr, div = s or 1
 // scaled by softmax_scale; causal, plus the window for NOPE/ROPE.
 //
 // Work decomposition. A workgroup (8 wavefronts, two per SIMD) owns 256 query
@@ -211,17 +214,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // second K row a thread stages is RPS keys after the first; when their
   // rotation ids differ by that step (RPS for base ids, RPS / s for remote ids
   // when s divides RPS) its cos/sin are the first row's times the step's.
-  __shared__ uint2 kfreq[CPR * 4];
+  __shared__ uint2 kfreq[2][CPR * 4];  // [0]: base frequencies, [1]: remote frequencies
   __shared__ float2 kstep[2][CPR * 4];
   const int id_step1 = NU > 1 ? RPS : -1;
   const int sdiv = static_cast<int>(a.scale_div.div);
   const int id_step2 = (NU > 1 && RPS % sdiv == 0) ? RPS / sdiv : -1;
   if (MODE != kNope && tid < CPR * 4) {
     const uint32_t flo = a.f.lo[tid], fhi = a.f.hi[tid];
-    kfreq[tid] = make_uint2(flo, fhi);
+    const uint32_t rlo = a.fr.lo[tid], rhi = a.fr.hi[tid];
+    kfreq[0][tid] = make_uint2(flo, fhi);
+    kfreq[1][tid] = make_uint2(rlo, rhi);
     float s1 = 0.f, c1 = 1.f, s2 = 0.f, c2 = 1.f;
     if (id_step1 >= 0) rope_sincos(id_step1, flo, fhi, s1, c1);
-    if (id_step2 >= 0) rope_sincos(id_step2, flo, fhi, s2, c2);
+    if (id_step2 >= 0) rope_sincos(id_step2, rlo, rhi, s2, c2);
     kstep[0][tid] = make_float2(c1, s1);
     kstep[1][tid] = make_float2(c2, s2);
   }
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         uint32_t kflo[4], kfhi[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint2 f = kfreq[sc * 4 + e];
+          const uint2 f = kfreq[rot - 1][sc * 4 + e];
           kflo[e] = f.x;
           kfhi[e] = f.y;
         }
@@ -325,10 +330,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       u32x4_t x = bload16(qres, qoff + ks * 32);  // rows past the sequence read 0
       if (MODE != kNope && rot) {
         uint32_t flo[4], fhi[4];
+        const RopeFreq& fq = rot == 2 ? a.fr : a.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          flo[e] = a.f.lo[ks * 8 + lg * 4 + e];
-          fhi[e] = a.f.hi[ks * 8 + lg * 4 + e];
+          flo[e] = fq.lo[ks * 8 + lg * 4 + e];
+          fhi[e] = fq.hi[ks * 8 + lg * 4 + e];
         }
         x = rotate_chunk(x, r, flo, fhi);
       }

@@ -67,7 +67,6 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
   }
 
   const int spair = tid % NPR;  // pair this thread stages (same for every row it stages)
-  const uint32_t sflo = a.f.lo[spair], sfhi = a.f.hi[spair];
 
   float o[DH], q[DH];
 #pragma unroll
@@ -78,6 +77,8 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     if (p >= npass) break;
+    const RopeFreq& fp = rot[p] == 2 ? a.fr : a.f;  // the remote pass may use interpolated frequencies
+    const uint32_t sflo = fp.lo[spair], sfhi = fp.hi[spair];
     // this lane's slice of the rotated query row for this pass
     const int rq = (valid && MODE != kNope && rot[p]) ? rot_index_f<MODE>(posb[i], rot[p], a) : 0;
 #pragma unroll
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
       float x1 = valid ? qg[size_t(i) * rowq + 2 * pe + 1] : 0.f;
       if (MODE != kNope && rot[p]) {
         float s, c;
-        rope_sincos(rq, a.f.lo[pe], a.f.hi[pe], s, c);
+        rope_sincos(rq, fp.lo[pe], fp.hi[pe], s, c);
         float y0, y1;
         rot_pair(x0, x1, c, s, y0, y1);
         x0 = y0;

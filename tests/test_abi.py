@@ -52,10 +52,11 @@ def test_group_size_golden():
 
 
 def _params(**kw):
-    d = dict(mode=P.BIFOCAL, period=0, remap_scale=2, window_left=8, rope_base=1e6, softmax_scale=0.0, w_pretrained=0)
+    d = dict(mode=P.BIFOCAL, period=0, remap_scale=2, window_left=8, rope_base=1e6, softmax_scale=0.0, w_pretrained=0,
+             remote_map=0)
     d.update(kw)
     return P.PropeParams(d["mode"], d["period"], d["remap_scale"], d["window_left"], d["rope_base"],
-                         d["softmax_scale"], d["w_pretrained"])
+                         d["softmax_scale"], d["w_pretrained"], d["remote_map"])
 
 
 def _prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos=FAKE, B=1, S=16, Hq=4, Hkv=2, d=128, dt=0,
@@ -79,6 +80,8 @@ def _prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos=FAKE, B=1, S=16, Hq=4
     dict(params=_params(softmax_scale=-1.0)), dict(params=_params(w_pretrained=-1)),
     dict(params=_params(w_pretrained=64)),                              # dynamic G needs remap_scale 1
     dict(params=_params(mode=P.ROPE, remap_scale=1, w_pretrained=64)),  # dynamic G is bifocal only
+    dict(params=_params(remote_map=2)), dict(params=_params(remote_map=-1)),
+    dict(params=_params(mode=P.ROPE, remap_scale=1, remote_map=1)),     # interpolation is bifocal only
     dict(byref=False),
 ])
 def test_prefill_rejects(kw):
@@ -106,6 +109,7 @@ def _decode(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, kv_len=FAKE, B=1, Lmax=4096, Hq=32
     (dict(dt=1), UNSUPPORTED), (dict(Hq=64, Hkv=2), UNSUPPORTED),
     (dict(Lmax=1 << 21, Hkv=8, Hq=32), UNSUPPORTED),
     (dict(ws_bytes=100), WORKSPACE),
+    (dict(params=_params(remap_scale=1, w_pretrained=4096, remote_map=1)), UNSUPPORTED),
 ])
 def test_decode_rejects(kw, code):
     assert _decode(**kw) == code
@@ -125,6 +129,7 @@ def _unfused(q=FAKE, k=FAKE, v=FAKE, o=FAKE, pos=FAKE, B=1, S=1000, Hq=4, Hkv=2,
     (dict(params=_params(mode=P.ROPE, remap_scale=1)), INVALID), (dict(params=_params(mode=P.NOPE, remap_scale=1)), INVALID),
     (dict(pos=None), INVALID), (dict(ws=None), INVALID), (dict(ws=FAKE + 16), INVALID),
     (dict(ws_bytes=1000), WORKSPACE), (dict(d=96), INVALID), (dict(Hq=5, Hkv=2), INVALID),
+    (dict(params=_params(remote_map=1)), UNSUPPORTED),
 ])
 def test_unfused_rejects(kw, code):
     assert _unfused(**kw) == code

@@ -141,6 +141,39 @@ def test_unfused_full_window_reduces_to_call_a():
     assert torch.equal(o_u, o_r)
 
 
+# ------------------------------------------------------------------ interpolated remote mapping
+
+INTERP = [
+    ("interp_gqa4", (1, 700, 8, 2, 128, "bf16"), dict(rope_base=1e6, remap_scale=2, window_left=150), None),
+    ("interp_s3_d64", (2, 333, 4, 2, 64, "bf16"), dict(rope_base=1e4, remap_scale=3, window_left=40), None),
+    ("interp_all_remote", (1, 260, 4, 1, 128, "bf16"), dict(rope_base=1e6, remap_scale=4, window_left=-1), None),
+    ("interp_huge_ids", (1, 300, 4, 2, 128, "bf16"), dict(rope_base=1e6, remap_scale=5, window_left=70),
+     (np.arange(300) + (1 << 20)).astype(np.int32)),
+    ("interp_fp32", (1, 150, 4, 2, 128, "fp32"), dict(rope_base=1e6, remap_scale=2, window_left=20), None),
+]
+
+
+@pytest.mark.parametrize("name,shape,kw,ids", INTERP, ids=[c[0] for c in INTERP])
+def test_interp_prefill_small(name, shape, kw, ids):
+    B, S, Hq, Hkv, d, dtype = shape
+    inp = _inputs(B, S, Hq, Hkv, d, dtype, seed=zlib.crc32(name.encode()) % 1000, ids=ids)
+    check_prefill(inp, "bifocal", dtype, what=name, remote_map="interp", **kw)
+
+
+def test_interp_decode_matches_prefill_last_row():
+    B, S, Hq, Hkv, d = 1, 900, 8, 2, 128
+    inp = _inputs(B, S, Hq, Hkv, d, "bf16", seed=35)
+    kw = dict(rope_base=1e6, remap_scale=3, window_left=120, remote_map="interp")
+    q, k, v, pos = (inp[n].cuda() for n in ("q", "k", "v", "pos"))
+    kc = P.rope_apply(k, pos, kw["rope_base"])
+    ql = P.rope_apply(q[:, -1:].contiguous(), pos[:, -1:].contiguous(), kw["rope_base"])[:, 0].contiguous()
+    o_dec = P.decode(ql, kc, v, torch.tensor([S], dtype=torch.int32).cuda(), mode="bifocal", **kw)
+    torch.cuda.synchronize()
+    o_pre, _ = O.prefill_ref(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), inp["pos"].numpy(), "bifocal",
+                             rows=[S - 1], **kw)
+    assert_close(to_np(o_dec), o_pre[:, 0], "bf16", "interp decode vs prefill oracle last row")
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def test_endprompt_fp32_full():
@@ -185,6 +218,11 @@ DEC_SMALL = [
     ("multi_chunk_s3_d64", (2, 4500, 16, 4, 64), "bifocal", dict(rope_base=1e6, remap_scale=3, window_left=1000),
      [4500, 4096]),
     ("multi_chunk_nope_window", (1, 5000, 8, 8, 128), "nope", dict(window_left=2100), [5000]),
+    # interpolated remote frequencies (Jet-Long section 4.5)
+    ("interp_multi_chunk", (3, 5000, 8, 2, 128), "bifocal",
+     dict(rope_base=1e6, remap_scale=4, window_left=300, remote_map="interp"), [5000, 1, 4097]),
+    ("interp_s3_d64", (2, 1500, 8, 2, 64), "bifocal",
+     dict(rope_base=1e4, remap_scale=3, window_left=0, remote_map="interp"), [1500, 513]),
 ]
 
 

@@ -443,3 +443,70 @@ def test_operand_rounding_identity_on_bf16_inputs():
     c, _ = O.prefill_ref(q, k, v, pos, "rope", operand_round="bf16")
     d_, _ = O.prefill_ref(q, k, v, pos, "rope")
     assert 0 < np.max(np.abs(c - d_)) < 0.05
+
+
+# ---------------------------------------------------------------- interpolated remote mapping
+# (Jet-Long page, section 4.5: remote view with frequencies theta_i / s at the
+# original positions instead of aliased positions floor(p / s))
+
+def test_interp_all_remote_equals_sdpa_on_complex_rotation():
+    # w0 = -1: every key remote; rotate at angle p * theta_i / s with complex
+    # multiplication (independent of O.rotate), then the library's SDPA
+    B, S, Hq, Hkv, d, base, s = 1, 27, 4, 2, 8, 1e6, 3
+    q, k, v = _rand_qkv(B, S, Hq, Hkv, d, 31)
+    pos = np.arange(S)[None] * 7 + 5
+    th = np.array([base ** (-(2 * i) / d) for i in range(d // 2)]) / s
+
+    def crot(x):
+        z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * pos[:, :, None, None] * th)
+        y = np.empty_like(x)
+        y[..., 0::2], y[..., 1::2] = z.real, z.imag
+        return y
+
+    o, _ = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=base, remap_scale=s, window_left=-1,
+                         remote_map="interp")
+    assert np.allclose(o, _sdpa(crot(q), crot(k), v, causal=True), atol=1e-12)
+
+
+def test_interp_vectorized_equals_brute_force():
+    B, S, Hq, Hkv, d = 1, 11, 2, 1, 6
+    q, k, v = _rand_qkv(B, S, Hq, Hkv, d, 32)
+    pos = np.arange(S)[None] + 3
+    o, _ = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=1e4, remap_scale=3, window_left=2,
+                         remote_map="interp")
+    bf = np.array(O.brute_force_prefill(q, k, v, pos, "bifocal", 1e4, remap_scale=3, window_left=2,
+                                        remote_map="interp"))
+    assert np.allclose(o, bf, atol=1e-12)
+
+
+def test_interp_scale_one_and_shift_invariance():
+    q, k, v = _rand_qkv(1, 25, 4, 2, 8, 33)
+    pos = np.arange(25)[None]
+    plain, _ = O.prefill_ref(q, k, v, pos, "rope", rope_base=1e6)
+    o1, _ = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=1e6, remap_scale=1, window_left=5,
+                          remote_map="interp")
+    assert np.allclose(o1, plain, atol=1e-12)
+    # unlike aliasing (invariant only under shifts by multiples of s), the
+    # interpolated view depends on id differences alone: any shift leaves it unchanged
+    o3, _ = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=1e6, remap_scale=3, window_left=5,
+                          remote_map="interp")
+    o3s, _ = O.prefill_ref(q, k, v, pos + 1001, "bifocal", rope_base=1e6, remap_scale=3, window_left=5,
+                           remote_map="interp")
+    assert np.allclose(o3, o3s, atol=1e-10)
+    oa, _ = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=1e6, remap_scale=3, window_left=5)
+    assert not np.allclose(o3, oa, atol=1e-6)  # a different mapping indeed
+
+
+@pytest.mark.parametrize("L,s,w0", [(40, 3, 7), (33, 4, -1)])
+def test_interp_decode_equals_last_prefill_row(L, s, w0):
+    B, Hq, Hkv, d, base = 1, 4, 2, 16, 1e6
+    q, k, v = _rand_qkv(B, L, Hq, Hkv, d, 34)
+    pos = np.tile(np.arange(L), (B, 1))
+    o_pre, l_pre = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=base, remap_scale=s, window_left=w0,
+                                 remote_map="interp")
+    kc = O.rope_apply_ref(k, pos, base)
+    ql = O.rope_apply_ref(q[:, -1:], pos[:, -1:], base)[:, 0]
+    o_dec, l_dec = O.decode_ref(ql, kc, v, np.full(B, L), "bifocal", rope_base=base, remap_scale=s,
+                                window_left=w0, remote_map="interp")
+    assert np.allclose(o_dec, o_pre[:, -1], atol=1e-10)
+    assert np.allclose(l_dec, l_pre[:, :, -1], atol=1e-10)
