@@ -141,6 +141,37 @@ def test_unfused_full_window_reduces_to_call_a():
     assert torch.equal(o_u, o_r)
 
 
+# ------------------------------------------------------------------ P-RoPE generation with a ring-buffer cache
+
+def test_prope_ring_buffer_generation():
+    """P-RoPE decode (P-RoPE page, section 3.2): keys rotated at phi(t) = t mod P are
+    kept in a W-slot ring buffer (slot t mod W, overwritten cyclically); the decode
+    at step t attends to the min(t+1, W) live slots, in any order, with no mask.
+    Each step equals row t of the direct windowed P-RoPE oracle."""
+    W, Pp, n = 128, 256, 420
+    Hq, Hkv, d, base = 8, 4, 128, 1e4
+    inp = _inputs(1, n, Hq, Hkv, d, "bf16", seed=91)
+    dev = torch.device("cuda:0")
+    q_all, k_all, v_all = (inp[x].to(dev) for x in ("q", "k", "v"))
+    kc = torch.zeros((1, W, Hkv, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    outs = {}
+    for t in range(n):
+        phi = torch.tensor([[t % Pp]], dtype=torch.int32, device=dev)
+        slot = t % W
+        P.rope_apply(k_all[:, t:t + 1].contiguous(), phi, base, out=kc[:, slot:slot + 1])
+        vc[:, slot] = v_all[:, t]
+        qt = P.rope_apply(q_all[:, t:t + 1].contiguous(), phi, base)[:, 0].contiguous()
+        outs[t] = P.decode(qt, kc, vc, torch.tensor([min(t + 1, W)], dtype=torch.int32, device=dev),
+                           mode="rope", rope_base=base, window_left=-1)
+    torch.cuda.synchronize()
+    checks = [0, 5, W - 2, W - 1, W, Pp - 1, Pp, Pp + W, n - 1]
+    ref, _ = O.prefill_ref(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), inp["pos"].numpy(), "rope",
+                           rope_base=base, period=Pp, window_left=W - 1, rows=checks)
+    for c, t in enumerate(checks):
+        assert_close(to_np(outs[t]), ref[:, c], "bf16", f"ring step t = {t}")
+
+
 # ------------------------------------------------------------------ interpolated remote mapping
 
 INTERP = [
