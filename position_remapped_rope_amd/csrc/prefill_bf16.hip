@@ -318,6 +318,105 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     }
   };
 
+  // Branch-free staging for the main loop, so that it shares one scheduling
+  // region with the MFMAs it is interleaved with. Tile indices past the last
+  // tile are harmless there: their loads stay inside the sequence's buffer
+  // resources, and the K/V buffers they overwrite are not read again. Row 1's
+  // cos/sin always come from the affine step; lanes whose ids break it are
+  // redone exactly by fix_row1 (outside the region).
+  bool need_fix = false;
+  // this thread's frequencies and row steps, in registers for both rotation kinds
+  uint2 kf_reg[2][4];
+  float2 ks_reg[2][4];
+  if (MODE != kNope) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf_reg[k][e] = kfreq[k][sc * 4 + e];
+        ks_reg[k][e] = kstep[k][sc * 4 + e];
+      }
+  }
+  auto stage_load_nb = [&](int tk, int tv) __attribute__((always_inline)) {
+    int p, kt;
+    tile_of(tk, p, kt);
+    const uint32_t j0 = uint32_t(kt) * kBN;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const uint32_t j = j0 + sr + RPS * u;
+      kraw[u] = bload16(kres, j * rowk_b + kcol_b);
+      kid[u] = MODE != kNope ? bload_i32(pres, j * 4) : 0;
+    }
+    int pv, ktv;
+    tile_of(tv, pv, ktv);
+    const uint32_t jv = uint32_t(ktv) * kBN;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) vraw[u] = bload16(vres, (jv + sr + RPS * u) * rowk_b + kcol_b);
+  };
+  auto stage_store_nb = [&](int tk, int tv) __attribute__((always_inline)) {
+    int p, kt;
+    tile_of(tk, p, kt);
+    uint16_t* dst = Ks[tk & 1];
+    if (MODE != kNope) {  // ROPE and BIFOCAL rotate in every pass (rot 1 or 2)
+      const int rot = p ? rot1 : rot0;
+      const int id_step = rot == 2 ? id_step2 : id_step1;
+      float cs[4], sn[4];
+      const int r0 = rot_index<MODE>(kid[0], rot, a);
+      const bool remote = rot == 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint2 f = remote ? kf_reg[1][e] : kf_reg[0][e];
+        rope_sincos(r0, f.x, f.y, sn[e], cs[e]);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if (u > 0) {
+          need_fix = !(id_step >= 0 && rot_index<MODE>(kid[u], rot, a) - r0 == id_step * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {  // (cs + i sn) * (step cos + i step sin)
+            const float2 es = remote ? ks_reg[1][e] : ks_reg[0][e];
+            const float c2 = cs[e] * es.x - sn[e] * es.y;
+            const float s2 = sn[e] * es.x + cs[e] * es.y;
+            cs[e] = c2;
+            sn[e] = s2;
+          }
+        }
+        u32x4_t y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float y0, y1;
+          rot_pair(bf16_lo(kraw[u][e]), bf16_hi(kraw[u][e]), cs[e], sn[e], y0, y1);
+          y[e] = pack_bf16(y0, y1);
+        }
+        *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = y;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = kraw[u];
+    }
+    uint16_t* vdst = Vs[tv & 1];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&vdst[(sr + RPS * u) * VRow + sc * 8]) = vraw[u];
+  };
+  auto fix_row1 = [&](int tk) __attribute__((always_inline)) {
+    if (MODE != kNope && NU > 1 && need_fix) {
+      int p, kt;
+      tile_of(tk, p, kt);
+      const int rot = p ? rot1 : rot0;
+      const int ru = rot_index<MODE>(kid[NU - 1], rot, a);
+      u32x4_t y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint2 f = kfreq[rot - 1][sc * 4 + e];
+        float sn, cs, y0, y1;
+        rope_sincos(ru, f.x, f.y, sn, cs);
+        rot_pair(bf16_lo(kraw[NU - 1][e]), bf16_hi(kraw[NU - 1][e]), cs, sn, y0, y1);
+        y[e] = pack_bf16(y0, y1);
+      }
+      *reinterpret_cast<u32x4_t*>(&Ks[tk & 1][(sr + RPS * (NU - 1)) * KRow + sc * 8]) = y;
+    }
+  };
+
   // ---- query operand (B of S^T = K Q^T): lane holds row lr, dims ks*16 + lg*8 .. +7
   u32x4_t qreg[KS];
   auto load_q = [&](int p) __attribute__((always_inline)) {
@@ -429,6 +528,119 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     }
   };
 
+  // Matrix phase of iteration t with the staging of K tile t+2 and V tile t+1
+  // woven between its 32 MFMAs: PV(t) (16 MFMAs), then QK(t+1) (16 MFMAs),
+  // each followed by one small piece of the staging work, with scheduling
+  // barriers keeping that order. While an MFMA runs, the wave issues the
+  // vector instructions of the next piece (RoPE of its K rows), so the RoPE
+  // no longer adds to the phase. Operand reads run one PV step / three QK
+  // steps ahead of their MFMAs.
+  auto mphase = [&](int t) __attribute__((always_inline)) {
+    const int tk = t + 2, tv = t + 1;
+    int pk, kt;
+    tile_of(tk, pk, kt);
+    const int rot = pk ? rot1 : rot0;
+    const bool remote = rot == 2;
+    const int id_step = remote ? id_step2 : id_step1;
+    uint16_t* kdst = &Ks[tk & 1][sr * KRow + sc * 8];
+    uint16_t* vdst = &Vs[tv & 1][sr * VRow + sc * 8];
+    int r0 = 0;
+    uint32_t ph[4];
+    float cs[4], sn[4], yv[2][8];
+    auto piece = [&](int i) __attribute__((always_inline)) {
+      if (MODE == kNope) {
+        if (i < NU) *reinterpret_cast<u32x4_t*>(kdst + RPS * i * KRow) = kraw[i];
+        else if (i < 2 * NU) *reinterpret_cast<u32x4_t*>(vdst + RPS * (i - NU) * VRow) = vraw[i - NU];
+        return;
+      }
+      if (i == 0) {
+        r0 = rot_index<MODE>(kid[0], rot, a);
+      } else if (i == 1) {
+        if (NU > 1) need_fix = !(id_step >= 0 && rot_index<MODE>(kid[NU - 1], rot, a) - r0 == id_step);
+      } else if (i >= 2 && i < 6) {
+        const int e = i - 2;
+        const uint2 f = remote ? kf_reg[1][e] : kf_reg[0][e];
+        ph[e] = phase_top(r0, f.x, f.y);
+      } else if (i >= 6 && i < 10) {
+        const int e = i - 6;
+        phase_sincos(ph[e], sn[e], cs[e]);
+      } else if (i >= 10 && i < 14) {
+        const int e = i - 10;
+        rot_pair(bf16_lo(kraw[0][e]), bf16_hi(kraw[0][e]), cs[e], sn[e], yv[0][2 * e], yv[0][2 * e + 1]);
+        if (e == 3) {
+          const u32x4_t y = {pack_bf16(yv[0][0], yv[0][1]), pack_bf16(yv[0][2], yv[0][3]),
+                             pack_bf16(yv[0][4], yv[0][5]), pack_bf16(yv[0][6], yv[0][7])};
+          *reinterpret_cast<u32x4_t*>(kdst) = y;
+        }
+      } else if (NU > 1 && i >= 14 && i < 18) {  // the second row: one affine step further
+        const int e = i - 14;
+        const float2 es = remote ? ks_reg[1][e] : ks_reg[0][e];
+        const float c2 = cs[e] * es.x - sn[e] * es.y;
+        const float s2 = sn[e] * es.x + cs[e] * es.y;
+        cs[e] = c2;
+        sn[e] = s2;
+      } else if (NU > 1 && i >= 18 && i < 22) {
+        const int e = i - 18;
+        rot_pair(bf16_lo(kraw[NU - 1][e]), bf16_hi(kraw[NU - 1][e]), cs[e], sn[e], yv[1][2 * e],
+                 yv[1][2 * e + 1]);
+        if (e == 3) {
+          const u32x4_t y = {pack_bf16(yv[1][0], yv[1][1]), pack_bf16(yv[1][2], yv[1][3]),
+                             pack_bf16(yv[1][4], yv[1][5]), pack_bf16(yv[1][6], yv[1][7])};
+          *reinterpret_cast<u32x4_t*>(kdst + RPS * (NU - 1) * KRow) = y;
+        }
+      } else if (i >= 22 && i < 22 + NU) {
+        *reinterpret_cast<u32x4_t*>(vdst + RPS * (i - 22) * VRow) = vraw[i - 22];
+      }
+    };
+    const uint16_t* vbase = &Vs[t & 1][vrow0 * VRow + vcol0];
+    const uint16_t* kbase = &Ks[(t + 1) & 1][lr * KRow + lg * 8];
+    u32x4_t vop[2][DB];
+    auto read_v = [&](int kk, u32x4_t* dst) __attribute__((always_inline)) {
+      const uint16_t* vrow = vbase + kk * 16 * VRow;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2_t va = lds_read_tr16(vrow + db * 32);
+        const u32x2_t vb = lds_read_tr16(vrow + 8 * VRow + db * 32);
+        dst[db] = u32x4_t{va[0], va[1], vb[0], vb[1]};
+      }
+    };
+    constexpr int KA = 3;  // K steps read ahead
+    u32x4_t kop[KA + 1][2];
+    auto read_k = [&](int ks, u32x4_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) dst[nb] = *reinterpret_cast<const u32x4_t*>(kbase + nb * 32 * KRow + ks * 16);
+    };
+    int pc = 0;  // next staging piece
+    read_v(0, vop[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) {
+        read_v(kk + 1, vop[(kk + 1) & 1]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KA; ++ks) read_k(ks, kop[ks]);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        oacc[db] = mfma32x32x16(vop[kk & 1][db], pop[kk], oacc[db]);
+        piece(pc++);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + KA < KS) read_k(ks + KA, kop[(ks + KA) % (KA + 1)]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        sacc[nb] = mfma32x32x16(kop[ks % (KA + 1)][nb], qreg[ks], ks == 0 ? f32x16_t{} : sacc[nb]);
+        piece(pc++);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (; pc < 24; ++pc) piece(pc);  // whatever is left (d = 64: fewer MFMAs)
+  };
+
   // vector phase of tile t: mask, online softmax, P -> bf16, lazy O rescale
   auto softmax_step = [&](int t) __attribute__((always_inline)) {
     bool need_mask;
@@ -510,13 +722,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   lds_barrier();
 #pragma clang loop unroll(disable)
   for (int t = 0; t < T; ++t) {
-    const bool lv = softmax_step(t);
+    softmax_step(t);  // P of a tile with no kept key is zero
     if (MODE == kBifocal && t + 1 < T && pass_of(t + 1) != pass_of(t)) load_q(pass_of(t + 1));
     lds_barrier();
-    if (lv) pv_step(t);
-    qk_or_clear(t + 1);
-    stage_store(t + 2, t + 1);
-    stage_load(t + 3, t + 2);
+    // one region: PV(t), QK(t+1) (the scores of tile T, if any, are never used)
+    // and the staging of K tile t+2 / V tile t+1, interleaved by the scheduler
+    mphase(t);
+    fix_row1(t + 2);
+    stage_load_nb(t + 3, t + 2);
     lds_barrier();
   }
   if (group == 0) lds_barrier();
