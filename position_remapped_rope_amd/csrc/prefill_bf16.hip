@@ -318,25 +318,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     }
   };
 
-  // Branch-free staging for the main loop, so that it shares one scheduling
-  // region with the MFMAs it is interleaved with. Tile indices past the last
-  // tile are harmless there: their loads stay inside the sequence's buffer
+  // Branch-free staging for the main loop (loads here, the rotation and LDS
+  // stores woven into the matrix phase below). Tile indices past the last tile
+  // are harmless there: their loads stay inside the sequence's buffer
   // resources, and the K/V buffers they overwrite are not read again. Row 1's
   // cos/sin always come from the affine step; lanes whose ids break it are
-  // redone exactly by fix_row1 (outside the region).
+  // redone exactly by fix_row1 (outside the woven region).
   bool need_fix = false;
-  // this thread's frequencies and row steps, in registers for both rotation kinds
-  uint2 kf_reg[2][4];
-  float2 ks_reg[2][4];
-  if (MODE != kNope) {
+  // this thread's frequencies and row steps for the rotation kind of the K
+  // tiles being staged, in registers (reloaded when that kind changes)
+  uint2 kf_reg[4];
+  float2 ks_reg[4];
+  int kreg_rot = -1;
+  auto load_kregs = [&](int rot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf_reg[k][e] = kfreq[k][sc * 4 + e];
-        ks_reg[k][e] = kstep[k][sc * 4 + e];
-      }
-  }
+    for (int e = 0; e < 4; ++e) {
+      kf_reg[e] = kfreq[rot - 1][sc * 4 + e];
+      ks_reg[e] = kstep[rot - 1][sc * 4 + e];
+    }
+    kreg_rot = rot;
+  };
   auto stage_load_nb = [&](int tk, int tv) __attribute__((always_inline)) {
     int p, kt;
     tile_of(tk, p, kt);
@@ -352,51 +353,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     const uint32_t jv = uint32_t(ktv) * kBN;
 #pragma unroll
     for (int u = 0; u < NU; ++u) vraw[u] = bload16(vres, (jv + sr + RPS * u) * rowk_b + kcol_b);
-  };
-  auto stage_store_nb = [&](int tk, int tv) __attribute__((always_inline)) {
-    int p, kt;
-    tile_of(tk, p, kt);
-    uint16_t* dst = Ks[tk & 1];
-    if (MODE != kNope) {  // ROPE and BIFOCAL rotate in every pass (rot 1 or 2)
-      const int rot = p ? rot1 : rot0;
-      const int id_step = rot == 2 ? id_step2 : id_step1;
-      float cs[4], sn[4];
-      const int r0 = rot_index<MODE>(kid[0], rot, a);
-      const bool remote = rot == 2;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint2 f = remote ? kf_reg[1][e] : kf_reg[0][e];
-        rope_sincos(r0, f.x, f.y, sn[e], cs[e]);
-      }
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        if (u > 0) {
-          need_fix = !(id_step >= 0 && rot_index<MODE>(kid[u], rot, a) - r0 == id_step * u);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {  // (cs + i sn) * (step cos + i step sin)
-            const float2 es = remote ? ks_reg[1][e] : ks_reg[0][e];
-            const float c2 = cs[e] * es.x - sn[e] * es.y;
-            const float s2 = sn[e] * es.x + cs[e] * es.y;
-            cs[e] = c2;
-            sn[e] = s2;
-          }
-        }
-        u32x4_t y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float y0, y1;
-          rot_pair(bf16_lo(kraw[u][e]), bf16_hi(kraw[u][e]), cs[e], sn[e], y0, y1);
-          y[e] = pack_bf16(y0, y1);
-        }
-        *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = y;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = kraw[u];
-    }
-    uint16_t* vdst = Vs[tv & 1];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&vdst[(sr + RPS * u) * VRow + sc * 8]) = vraw[u];
   };
   auto fix_row1 = [&](int tk) __attribute__((always_inline)) {
     if (MODE != kNope && NU > 1 && need_fix) {
@@ -540,8 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     int pk, kt;
     tile_of(tk, pk, kt);
     const int rot = pk ? rot1 : rot0;
-    const bool remote = rot == 2;
-    const int id_step = remote ? id_step2 : id_step1;
+    const int id_step = rot == 2 ? id_step2 : id_step1;
     uint16_t* kdst = &Ks[tk & 1][sr * KRow + sc * 8];
     uint16_t* vdst = &Vs[tv & 1][sr * VRow + sc * 8];
     int r0 = 0;
@@ -559,8 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         if (NU > 1) need_fix = !(id_step >= 0 && rot_index<MODE>(kid[NU - 1], rot, a) - r0 == id_step);
       } else if (i >= 2 && i < 6) {
         const int e = i - 2;
-        const uint2 f = remote ? kf_reg[1][e] : kf_reg[0][e];
-        ph[e] = phase_top(r0, f.x, f.y);
+        ph[e] = phase_top(r0, kf_reg[e].x, kf_reg[e].y);
       } else if (i >= 6 && i < 10) {
         const int e = i - 6;
         phase_sincos(ph[e], sn[e], cs[e]);
@@ -574,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         }
       } else if (NU > 1 && i >= 14 && i < 18) {  // the second row: one affine step further
         const int e = i - 14;
-        const float2 es = remote ? ks_reg[1][e] : ks_reg[0][e];
+        const float2 es = ks_reg[e];
         const float c2 = cs[e] * es.x - sn[e] * es.y;
         const float s2 = sn[e] * es.x + cs[e] * es.y;
         cs[e] = c2;
@@ -723,6 +677,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma clang loop unroll(disable)
   for (int t = 0; t < T; ++t) {
     softmax_step(t);  // P of a tile with no kept key is zero
+    if (MODE != kNope) {
+      const int srot = pass_of(t + 2) ? rot1 : rot0;
+      if (srot != kreg_rot) load_kregs(srot);
+    }
     if (MODE == kBifocal && t + 1 < T && pass_of(t + 1) != pass_of(t)) load_q(pass_of(t + 1));
     lds_barrier();
     // one region: PV(t), QK(t+1) (the scores of tile T, if any, are never used)
