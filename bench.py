@@ -191,7 +191,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=640)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--only", choices=["prefill_64k", "prefill_128k", "prefill_64k_unfused", "decode_b1", "decode_b8", "copy"],
                     help="time one leg only and print its figures (for profiler runs)")
     args = ap.parse_args()
