@@ -342,12 +342,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     int p, kt;
     tile_of(tk, p, kt);
     const uint32_t j0 = uint32_t(kt) * kBN;
+    // issue order = use order in the next matrix phase (ids, K rows, V rows), so
+    // each use waits only for its own loads
+    if (MODE != kNope) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const uint32_t j = j0 + sr + RPS * u;
-      kraw[u] = bload16(kres, j * rowk_b + kcol_b);
-      kid[u] = MODE != kNope ? bload_i32(pres, j * 4) : 0;
+      for (int u = 0; u < NU; ++u) kid[u] = bload_i32(pres, (j0 + sr + RPS * u) * 4);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) kraw[u] = bload16(kres, (j0 + sr + RPS * u) * rowk_b + kcol_b);
+    __builtin_amdgcn_sched_barrier(0);
     int pv, ktv;
     tile_of(tv, pv, ktv);
     const uint32_t jv = uint32_t(ktv) * kBN;
@@ -672,7 +676,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   if (group == 1) lds_barrier();
   qk_or_clear(0);
   stage_store(1, 0);
-  stage_load(2, 1);
+  stage_load_nb(2, 1);  // same issue order as in the loop, so the loads keep exact wait counts
   lds_barrier();
 #pragma clang loop unroll(disable)
   for (int t = 0; t < T; ++t) {
@@ -685,9 +689,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     lds_barrier();
     // one region: PV(t), QK(t+1) (the scores of tile T, if any, are never used)
     // and the staging of K tile t+2 / V tile t+1, interleaved by the scheduler
+    // The matrix phase runs at raised wave priority: its MFMAs and the staging
+    // between them are the longer stream, so the SIMD's arbiter gives it issue
+    // slots first and the other wave's softmax fills the gaps.
+    __builtin_amdgcn_s_setprio(1);
     mphase(t);
     fix_row1(t + 2);
     stage_load_nb(t + 3, t + 2);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
   }
   if (group == 0) lds_barrier();
