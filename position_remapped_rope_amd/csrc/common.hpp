@@ -32,6 +32,11 @@ __device__ __forceinline__ uint32_t phase_top(int32_t r, uint32_t flo, uint32_t 
   return top;
 }
 
+// The same for r >= 0 (prefill ids): no sign correction.
+__device__ __forceinline__ uint32_t phase_top_u(uint32_t r, uint32_t flo, uint32_t fhi) {
+  return __umulhi(r, flo) + r * fhi;
+}
+
 // sin and cos of 2*pi*t for t in [-1/2, 1/2) (v_sin_f32 / v_cos_f32 take revolutions).
 __device__ __forceinline__ void sincos_turns(float t, float& s, float& c) {
   s = __builtin_amdgcn_sinf(t);

@@ -177,17 +177,17 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const __amdgpu_buffer_rsrc_t vres = make_rsrc(static_cast<const uint16_t*>(a.v) + bofs, span);
 
   u32x4_t kraw[2][KSTEPS], vraw[VPL];
-  auto load_step = [&](int j0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        kraw[blk][ks] = bload16(kres, uint32_t(j0 + 16 * blk + kl) * rowk_b + (8 * kg + 32 * ks) * 2);
+  auto load_v = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < VPL; ++u) {
       const int c = lane + 64 * u;  // chunk c: key c / (D/8), 16-byte column c % (D/8)
       vraw[u] = bload16(vres, uint32_t(j0 + c / (D / 8)) * rowk_b + (c % (D / 8)) * 16);
     }
+  };
+  auto load_k = [&](int j0, int blk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      kraw[blk][ks] = bload16(kres, uint32_t(j0 + 16 * blk + kl) * rowk_b + (8 * kg + 32 * ks) * 2);
   };
 
   float m_run = -INFINITY, l_run = 0.f;  // per head kl (replicated over the 4 lane groups)
@@ -198,14 +198,23 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const int trow = 4 * kg + (kl >> 2);  // transposing-read row of this lane (block 0)
   const int tcol = 4 * (kl & 3);        // and column offset within a 16-dim block
 
-  if (wbeg < wend) load_step(wbeg);
+  // Loads of the next step go out as soon as the registers they fill are free:
+  // V right after this step's V is in LDS, each K block right after its scores,
+  // so their latency overlaps this step's rotation and MFMA work.
+  if (wbeg < wend) {
+    load_v(wbeg);
+    load_k(wbeg, 0);
+    load_k(wbeg, 1);
+  }
   for (int j0 = wbeg; j0 < wend; j0 += kStep) {
+    const bool more = j0 + kStep < wend;
     // -- V of this step to LDS (row-major); read back transposed after the scores
 #pragma unroll
     for (int u = 0; u < VPL; ++u) {
       const int c = lane + 64 * u;
       *reinterpret_cast<u32x4_t*>(&vt[(c / (D / 8)) * VROW + (c % (D / 8)) * 8]) = vraw[u];
     }
+    if (more) load_v(j0 + kStep);
     // -- scores S^T (keys x heads) for the two 16-key blocks
     f32x4_t sc[2];
 #pragma unroll
@@ -255,9 +264,8 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
         const bool keep = j < wend && (MODE == kBifocal || w0 < 0 || dist <= w0);
         sc[blk][i] = keep ? v * sl2 : -INFINITY;
       }
+      if (more) load_k(j0 + kStep, blk);
     }
-    // prefetch the next step while this one is processed
-    if (j0 + kStep < wend) load_step(j0 + kStep);
     if (MODE == kBifocal && affine) {  // the lane's block-0 key moves by 32
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
@@ -336,76 +344,74 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   }
 }
 
-// One workgroup per (query head, sequence). Threads split the chunk partials
-// (max, sum) and, for O, pairs of (chunk group, 4 dims), then reduce in LDS.
+// One workgroup per (query head, sequence), one round of loads: thread
+// (cg, dv) takes chunks cg, cg + CG, ... and 4 dims of O, merges them against
+// its own running max as it goes (the same log-sum-exp algebra as the split
+// kernel), and the CG partial merges are combined once in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a) {
   constexpr int NT = 256;
   constexpr int DV = D / 4;       // float4 columns per partial
-  constexpr int CG = NT / DV;     // chunk groups for the O reduction
-  __shared__ float red[NT];
-  __shared__ float4 ored[CG][DV];
+  constexpr int CG = NT / DV;     // chunk groups
+  __shared__ float sm[CG], sl[CG];
+  __shared__ float4 so[CG][DV];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
   const int nc = (L + a.chunk - 1) / a.chunk;
   const size_t stride = D + 2;
   const float* wsb = a.ws + (size_t(b) * a.Hq + h) * size_t(a.n_chunks) * stride;
-
-  float mx = -INFINITY;
-  for (int c = tid; c < nc; c += NT) mx = fmaxf(mx, wsb[size_t(c) * stride]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int off = NT / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  const float Mref = M == -INFINITY ? 0.f : M;
-  __syncthreads();
-
-  float ls = 0.f;
-  for (int c = tid; c < nc; c += NT)
-    ls = fmaf(__builtin_amdgcn_exp2f(wsb[size_t(c) * stride] - Mref), wsb[size_t(c) * stride + 1], ls);
-  red[tid] = ls;
-  __syncthreads();
-  for (int off = NT / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float lsum = red[0];
-
   const int dv = tid % DV, cg = tid / DV;
+
+  float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int c = cg; c < nc; c += CG) {
     const float* part = wsb + size_t(c) * stride;
-    const float w = __builtin_amdgcn_exp2f(part[0] - Mref);
+    const float mc = part[0], lc = part[1];
     // partial O starts at float offset 2: read as two float2 to stay 8-byte aligned
     const float2 x0 = *reinterpret_cast<const float2*>(part + 2 + 4 * dv);
     const float2 x1 = *reinterpret_cast<const float2*>(part + 4 + 4 * dv);
-    acc.x = fmaf(w, x0.x, acc.x);
-    acc.y = fmaf(w, x0.y, acc.y);
-    acc.z = fmaf(w, x1.x, acc.z);
-    acc.w = fmaf(w, x1.y, acc.w);
+    const float mn = fmaxf(m, mc);
+    if (mn == -INFINITY) continue;  // nothing kept so far
+    const float wo = __builtin_amdgcn_exp2f(m - mn), wc = __builtin_amdgcn_exp2f(mc - mn);
+    l = l * wo + lc * wc;
+    acc.x = acc.x * wo + x0.x * wc;
+    acc.y = acc.y * wo + x0.y * wc;
+    acc.z = acc.z * wo + x1.x * wc;
+    acc.w = acc.w * wo + x1.y * wc;
+    m = mn;
   }
-  ored[cg][dv] = acc;
+  so[cg][dv] = acc;
+  if (dv == 0) {
+    sm[cg] = m;
+    sl[cg] = l;
+  }
   __syncthreads();
   if (tid < DV) {
-    float4 t = ored[0][tid];
-    for (int g = 1; g < CG; ++g) {
-      t.x += ored[g][tid].x;
-      t.y += ored[g][tid].y;
-      t.z += ored[g][tid].z;
-      t.w += ored[g][tid].w;
+    float M = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < CG; ++g) M = fmaxf(M, sm[g]);
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float lsum = 0.f;
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int g = 0; g < CG; ++g) {
+      const float w = __builtin_amdgcn_exp2f(sm[g] - Mref);
+      lsum = fmaf(w, sl[g], lsum);
+      const float4 o = so[g][tid];
+      t.x = fmaf(w, o.x, t.x);
+      t.y = fmaf(w, o.y, t.y);
+      t.z = fmaf(w, o.z, t.z);
+      t.w = fmaf(w, o.w, t.w);
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     uint2 packed;
     packed.x = pack_bf16(t.x * inv, t.y * inv);
     packed.y = pack_bf16(t.z * inv, t.w * inv);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + (size_t(b) * a.Hq + h) * D + 4 * tid) = packed;
+    if (a.lse && tid == 0)
+      a.lse[size_t(b) * a.Hq + h] = lsum > 0.f ? (M + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
   }
-  if (a.lse && tid == 0)
-    a.lse[size_t(b) * a.Hq + h] = lsum > 0.f ? (M + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
 }
 
 template <int D, int MODE>

@@ -518,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         if (NU > 1) need_fix = !(id_step >= 0 && rot_index<MODE>(kid[NU - 1], rot, a) - r0 == id_step);
       } else if (i >= 2 && i < 6) {
         const int e = i - 2;
-        ph[e] = phase_top(r0, kf_reg[e].x, kf_reg[e].y);
+        ph[e] = phase_top_u(static_cast<uint32_t>(r0), kf_reg[e].x, kf_reg[e].y);
       } else if (i >= 6 && i < 10) {
         const int e = i - 6;
         phase_sincos(ph[e], sn[e], cs[e]);
