@@ -34,13 +34,14 @@
 //
 // Schedule (two wave groups in antiphase). Waves 0-3 (group 0) and 4-7
 // (group 1) put one wave of each group on every SIMD. Every wave alternates a
-// matrix phase (O += P V for tile t, then S = K Q^T for tile t+1: 32 MFMAs)
-// followed by its share of the K/V staging (RoPE of K rows, LDS stores), and
-// a vector phase (mask, online softmax and P packing for tile t+1). Group 1
-// runs one phase behind group 0, and a workgroup barrier separates phases, so
-// on each SIMD one wave's MFMAs and staging overlap the other wave's softmax.
-// K and V tiles are double-buffered in LDS; each group stages half of every
-// tile's rows, with the global loads issued one phase pair ahead.
+// matrix phase (O += P V for tile t, then S = K Q^T for tile t+1: 32 MFMAs,
+// with its share of the K/V LDS stores between them) and a vector phase (mask,
+// online softmax and P packing for tile t+1, interleaved with the RoPE of the
+// K rows it stores next). Group 1 runs one phase behind group 0, and a
+// workgroup barrier separates phases, so on each SIMD one wave's MFMAs overlap
+// the other wave's vector work. K and V tiles are double-buffered in LDS; each
+// group stages half of every tile's rows, with the global loads issued one
+// phase pair ahead.
 #include <limits.h>
 
 #include "internal.hpp"
@@ -318,12 +319,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     }
   };
 
-  // Branch-free staging for the main loop (loads here, the rotation and LDS
-  // stores woven into the matrix phase below). Tile indices past the last tile
-  // are harmless there: their loads stay inside the sequence's buffer
-  // resources, and the K/V buffers they overwrite are not read again. Row 1's
-  // cos/sin always come from the affine step; lanes whose ids break it are
-  // redone exactly by fix_row1 (outside the woven region).
+  // Branch-free staging for the main loop (loads here, the rotation in the
+  // vector phase, the LDS stores between the MFMAs of the matrix phase). Tile
+  // indices past the last tile are harmless there: their loads stay inside the
+  // sequence's buffer resources, and the K/V buffers they overwrite are not read
+  // again. Row 1's cos/sin always come from the affine step; lanes whose ids
+  // break it are redone exactly by fix_row1 after the matrix phase.
   bool need_fix = false;
   // this thread's frequencies and row steps for the rotation kind of the K
   // tiles being staged, in registers (reloaded when that kind changes)
@@ -342,8 +343,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     int p, kt;
     tile_of(tk, p, kt);
     const uint32_t j0 = uint32_t(kt) * kBN;
-    // issue order = use order in the next matrix phase (ids, K rows, V rows), so
-    // each use waits only for its own loads
+    // issue order = use order (ids, K rows, V rows), so each use waits only for
+    // its own loads
     if (MODE != kNope) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) kid[u] = bload_i32(pres, (j0 + sr + RPS * u) * 4);
@@ -488,67 +489,49 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     }
   };
 
-  // Matrix phase of iteration t with the staging of K tile t+2 and V tile t+1
-  // woven between its 32 MFMAs: PV(t) (16 MFMAs), then QK(t+1) (16 MFMAs),
-  // each followed by one small piece of the staging work, with scheduling
-  // barriers keeping that order. While an MFMA runs, the wave issues the
-  // vector instructions of the next piece (RoPE of its K rows), so the RoPE
-  // no longer adds to the phase. Operand reads run one PV step / three QK
-  // steps ahead of their MFMAs.
-  auto mphase = [&](int t) __attribute__((always_inline)) {
-    const int tk = t + 2, tv = t + 1;
+  // RoPE of the K rows a thread stages for tile t + 2, done during the vector
+  // phase of tile t: the rotation index, the exact phase (quarter-rate integer
+  // multiplies), sin/cos and the pair rotations are independent of the softmax,
+  // so they fill its dependency gaps, and the matrix phase is left with the
+  // LDS stores. The raw rows arrived during the previous matrix phase.
+  u32x4_t krot[NU];
+  auto rotate_k = [&](int t) __attribute__((always_inline)) {
+    if (MODE == kNope) return;
     int pk, kt;
-    tile_of(tk, pk, kt);
+    tile_of(t + 2, pk, kt);
     const int rot = pk ? rot1 : rot0;
     const int id_step = rot == 2 ? id_step2 : id_step1;
+    const int r0 = rot_index<MODE>(kid[0], rot, a);
+    if (NU > 1) need_fix = !(id_step >= 0 && rot_index<MODE>(kid[NU - 1], rot, a) - r0 == id_step);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float sn, cs, y0, y1;
+      phase_sincos(phase_top_u(static_cast<uint32_t>(r0), kf_reg[e].x, kf_reg[e].y), sn, cs);
+      rot_pair(bf16_lo(kraw[0][e]), bf16_hi(kraw[0][e]), cs, sn, y0, y1);
+      krot[0][e] = pack_bf16(y0, y1);
+      if (NU > 1) {  // the second row: one id step further, (cs + i sn) * (step cos + i step sin)
+        const float2 es = ks_reg[e];
+        const float c2 = cs * es.x - sn * es.y, s2 = sn * es.x + cs * es.y;
+        rot_pair(bf16_lo(kraw[NU - 1][e]), bf16_hi(kraw[NU - 1][e]), c2, s2, y0, y1);
+        krot[NU - 1][e] = pack_bf16(y0, y1);
+      }
+    }
+  };
+  // Matrix phase of iteration t: PV(t) (16 MFMAs), then QK(t+1) (16 MFMAs),
+  // with the LDS stores of this thread's rows of K tile t+2 and V tile t+1 one
+  // per MFMA slot, scheduling barriers keeping that order. Operand reads run
+  // one PV step / three QK steps ahead of their MFMAs.
+  auto mphase = [&](int t) __attribute__((always_inline)) {
+    const int tk = t + 2, tv = t + 1;
     uint16_t* kdst = &Ks[tk & 1][sr * KRow + sc * 8];
     uint16_t* vdst = &Vs[tv & 1][sr * VRow + sc * 8];
-    int r0 = 0;
-    uint32_t ph[4];
-    float cs[4], sn[4], yv[2][8];
+    // staging stores, one per MFMA slot: K rows (rotated in the vector phase,
+    // or raw for NoPE), then V rows
     auto piece = [&](int i) __attribute__((always_inline)) {
-      if (MODE == kNope) {
-        if (i < NU) *reinterpret_cast<u32x4_t*>(kdst + RPS * i * KRow) = kraw[i];
-        else if (i < 2 * NU) *reinterpret_cast<u32x4_t*>(vdst + RPS * (i - NU) * VRow) = vraw[i - NU];
-        return;
-      }
-      if (i == 0) {
-        r0 = rot_index<MODE>(kid[0], rot, a);
-      } else if (i == 1) {
-        if (NU > 1) need_fix = !(id_step >= 0 && rot_index<MODE>(kid[NU - 1], rot, a) - r0 == id_step);
-      } else if (i >= 2 && i < 6) {
-        const int e = i - 2;
-        ph[e] = phase_top_u(static_cast<uint32_t>(r0), kf_reg[e].x, kf_reg[e].y);
-      } else if (i >= 6 && i < 10) {
-        const int e = i - 6;
-        phase_sincos(ph[e], sn[e], cs[e]);
-      } else if (i >= 10 && i < 14) {
-        const int e = i - 10;
-        rot_pair(bf16_lo(kraw[0][e]), bf16_hi(kraw[0][e]), cs[e], sn[e], yv[0][2 * e], yv[0][2 * e + 1]);
-        if (e == 3) {
-          const u32x4_t y = {pack_bf16(yv[0][0], yv[0][1]), pack_bf16(yv[0][2], yv[0][3]),
-                             pack_bf16(yv[0][4], yv[0][5]), pack_bf16(yv[0][6], yv[0][7])};
-          *reinterpret_cast<u32x4_t*>(kdst) = y;
-        }
-      } else if (NU > 1 && i >= 14 && i < 18) {  // the second row: one affine step further
-        const int e = i - 14;
-        const float2 es = ks_reg[e];
-        const float c2 = cs[e] * es.x - sn[e] * es.y;
-        const float s2 = sn[e] * es.x + cs[e] * es.y;
-        cs[e] = c2;
-        sn[e] = s2;
-      } else if (NU > 1 && i >= 18 && i < 22) {
-        const int e = i - 18;
-        rot_pair(bf16_lo(kraw[NU - 1][e]), bf16_hi(kraw[NU - 1][e]), cs[e], sn[e], yv[1][2 * e],
-                 yv[1][2 * e + 1]);
-        if (e == 3) {
-          const u32x4_t y = {pack_bf16(yv[1][0], yv[1][1]), pack_bf16(yv[1][2], yv[1][3]),
-                             pack_bf16(yv[1][4], yv[1][5]), pack_bf16(yv[1][6], yv[1][7])};
-          *reinterpret_cast<u32x4_t*>(kdst + RPS * (NU - 1) * KRow) = y;
-        }
-      } else if (i >= 22 && i < 22 + NU) {
-        *reinterpret_cast<u32x4_t*>(vdst + RPS * (i - 22) * VRow) = vraw[i - 22];
-      }
+      if (i < NU)
+        *reinterpret_cast<u32x4_t*>(kdst + RPS * i * KRow) = MODE == kNope ? kraw[i] : krot[i];
+      else if (i < 2 * NU)
+        *reinterpret_cast<u32x4_t*>(vdst + RPS * (i - NU) * VRow) = vraw[i - NU];
     };
     const uint16_t* vbase = &Vs[t & 1][vrow0 * VRow + vcol0];
     const uint16_t* kbase = &Ks[(t + 1) & 1][lr * KRow + lg * 8];
@@ -596,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       }
     }
 #pragma unroll
-    for (; pc < 24; ++pc) piece(pc);  // whatever is left (d = 64: fewer MFMAs)
+    for (; pc < 2 * NU; ++pc) piece(pc);  // whatever is left
   };
 
   // vector phase of tile t: mask, online softmax, P -> bf16, lazy O rescale
@@ -606,6 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     if (!wave_live(t, need_mask, dlo, dhi, j0)) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) pop[kk] = u32x4_t{0, 0, 0, 0};
+      rotate_k(t);
       return false;
     }
     if (need_mask) {
@@ -625,6 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       mx1 = fmaxf(mx1, fmaxf(sacc[1][r], sacc[1][r + 1]));
     }
     const float mx = xhalf_max(fmaxf(mx0, mx1)) * sl2;
+    rotate_k(t);
     // The reference max moves only when the tile's max exceeds it by more than
     // 8 (log2 units): P <= 2^8 stays exact in bf16 and fp32, and O and l are
     // rescaled far less often. The final O / l and LSE = m + log2 l are unchanged.
@@ -669,10 +654,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // ---- phases -----------------------------------------------------------------
   // Group 0: QK(0) | soft(0) | PV(0) QK(1) | soft(1) | PV(1) QK(2) | ... | PV(T-1) | -
   // Group 1:  -    | QK(0)   | soft(0)     | PV(0) QK(1) | ...         | PV(T-1)
-  // with a workgroup barrier after every phase. After its MFMAs for tile t
-  // (PV(t), QK(t+1)) a wave stores its half of K tile t+2 and V tile t+1 to
-  // LDS and issues the loads of K tile t+3 and V tile t+2, so the RoPE work
-  // of the staging runs while the other wave of the SIMD is in its softmax.
+  // with a workgroup barrier after every phase. The vector phase of tile t
+  // also rotates this wave's rows of K tile t+2; the matrix phase after it
+  // stores them and its rows of V tile t+1 to LDS between its MFMAs, then
+  // issues the loads of K tile t+3 and V tile t+2.
   if (group == 1) lds_barrier();
   qk_or_clear(0);
   stage_store(1, 0);
@@ -680,18 +665,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   lds_barrier();
 #pragma clang loop unroll(disable)
   for (int t = 0; t < T; ++t) {
-    softmax_step(t);  // P of a tile with no kept key is zero
     if (MODE != kNope) {
       const int srot = pass_of(t + 2) ? rot1 : rot0;
       if (srot != kreg_rot) load_kregs(srot);
     }
+    softmax_step(t);  // P of a tile with no kept key is zero
     if (MODE == kBifocal && t + 1 < T && pass_of(t + 1) != pass_of(t)) load_q(pass_of(t + 1));
     lds_barrier();
     // one region: PV(t), QK(t+1) (the scores of tile T, if any, are never used)
-    // and the staging of K tile t+2 / V tile t+1, interleaved by the scheduler
-    // The matrix phase runs at raised wave priority: its MFMAs and the staging
-    // between them are the longer stream, so the SIMD's arbiter gives it issue
-    // slots first and the other wave's softmax fills the gaps.
+    // and the LDS stores of K tile t+2 / V tile t+1 between the MFMAs. It runs
+    // at raised wave priority: the SIMD's arbiter gives the MFMA stream its
+    // issue slots first and the other wave's vector work fills the gaps.
     __builtin_amdgcn_s_setprio(1);
     mphase(t);
     fix_row1(t + 2);
