@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill attn TFLOP/s (% bf16 MFMA peak) at 64K/128K; decode KV GB/s at 128K"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector ALU (the fp32 prefill path)
 
 
 def log(msg):
@@ -94,7 +95,13 @@ def bench_prefill(name, steps, warmup, unfused=False):
     dev = torch.device("cuda:0")
     q, k, v, pos = (inp[n].to(dev) for n in ("q", "k", "v", "pos"))
     o = torch.empty_like(q)
-    kw = dict(rope_base=w.rope_base, remap_scale=w.remap_scale, window_left=w.window_left)
+    if w.mode == "bifocal":
+        kw = dict(rope_base=w.rope_base, remap_scale=w.remap_scale, window_left=w.window_left)
+    elif w.mode == "rope":
+        kw = dict(rope_base=w.rope_base, period=w.period, window_left=w.window_left)
+    else:
+        kw = dict(window_left=w.window_left)
+        pos = None
 
     if unfused:  # the pages' three-call construction merged by Eq. (7), for comparison
         ws = torch.empty(P.bifocal_unfused_workspace_size(w.B, w.S, w.Hq, w.d), dtype=torch.uint8, device=dev)
@@ -103,15 +110,15 @@ def bench_prefill(name, steps, warmup, unfused=False):
             P.prefill_bifocal_unfused(q, k, v, pos, out=o, workspace=ws, **kw)
     else:
         def step(_):
-            P.prefill(q, k, v, pos, mode="bifocal", out=o, **kw)
+            P.prefill(q, k, v, pos, mode=w.mode, out=o, **kw)
 
     log(f"{name}: timing {steps} launches" + (" (unfused)" if unfused else ""))
     ms, wall = time_launches(step, steps, warmup)
     flops = prefill_flops(w)
     avg = sum(ms) / len(ms)
     tflops = flops / (avg * 1e-3) / 1e12
-    return w, inp, dict(ms=ms, avg_ms=avg, wall_s=wall, flops=flops, tflops=tflops,
-                        frac=tflops / PEAK_BF16_TFLOPS)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
+    return w, inp, dict(ms=ms, avg_ms=avg, wall_s=wall, flops=flops, tflops=tflops, frac=tflops / peak)
 
 
 def bench_decode(name, steps, warmup):
@@ -252,6 +259,12 @@ def main():
         _, _, unf = bench_prefill("bifocal_64k", max(3, args.steps // 2), 1, unfused=True)
         extra["bifocal_64k_unfused_eq7"] = {"tflops": round(unf["tflops"], 2), "avg_ms": round(unf["avg_ms"], 3),
                                             "fused_speedup": round(unf["avg_ms"] / pre["avg_ms"], 3)}
+        # the other prefill workloads: P-RoPE local + NoPE global layers at 8K, EndPrompt in fp32
+        for name, st in (("prope_local_8k", 20), ("nope_global_8k", 20), ("endprompt_fp32", 50)):
+            _, _, r = bench_prefill(name, st, 3)
+            extra[name] = {"tflops": round(r["tflops"], 2), "avg_ms": round(r["avg_ms"], 4), "flop": r["flops"],
+                           "frac_peak": round(r["frac"], 4),
+                           "peak": "bf16 MFMA 2500" if name != "endprompt_fp32" else "fp32 vector 157.3"}
         for name, st in (("bifocal_decode_128k_b1", 50), ("bifocal_decode_128k_b8", 10)):
             d = bench_decode(name, st, 3)
             extra[name] = {"gbs": round(d["gbs"], 1), "frac_hbm_peak": round(d["frac"], 4),

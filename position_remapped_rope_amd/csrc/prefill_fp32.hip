@@ -1,8 +1,11 @@
 // float32 prefill: same scores, masks and bifocal routing as the bf16 kernel,
-// computed with fp32 vector ALU (no operand rounding). One thread owns one
-// query row of one head; K (rotated in fp32) and V tiles of 32 keys are staged
-// in LDS and read as broadcasts. Meant for small fp32 problems such as the
-// EndPrompt two-segment check; the bf16 MFMA kernel is the throughput path.
+// computed with fp32 vector ALU (no operand rounding). D / 8 adjacent lanes
+// share one query row of one head, 8 dims each, and reduce each score with
+// lane shuffles; K (rotated in fp32) and V tiles of 32 keys are staged in LDS,
+// the next tile's loads in flight while the current one is processed.
+// Meant for small fp32 problems such as the EndPrompt two-segment check: the
+// narrow row split gives a 256-token problem enough workgroups to spread over
+// the chip. The bf16 MFMA kernel is the throughput path.
 #include <limits.h>
 
 #include "internal.hpp"
@@ -20,12 +23,12 @@ __device__ __forceinline__ int rot_index_f(int p, int rot, const PrefillArgs& a)
   return p;
 }
 
-// TPR = D / 64 lanes share one query row, each owning 64 of its dims; a
+// TPR = D / 8 lanes share one query row, each owning 8 of its dims; a
 // workgroup covers 256 / TPR rows (HG heads x BMp positions, set by the launcher).
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillArgs a) {
-  constexpr int TPR = D / 64;                      // lanes per query row
-  constexpr int DH = 64;                           // dims per lane
+  constexpr int DH = 8;                            // dims per lane
+  constexpr int TPR = D / DH;                      // lanes per query row
   constexpr int NPR = D / 2;                       // pairs per row
   constexpr int PAIRS = kBNf * NPR / kThreadsF;    // pairs staged per thread
   constexpr int RPS = kThreadsF / NPR;             // rows per staging sweep
@@ -100,33 +103,45 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
     const int64_t jlo = max<int64_t>(0, int64_t(P0) - dhi[p]);
     const int64_t jhi = min<int64_t>(S - 1, int64_t(P1) - dlo[p]);
     if (jhi < jlo) continue;
-    for (int j0 = static_cast<int>(jlo / kBNf) * kBNf; j0 <= jhi; j0 += kBNf) {
+    // this thread's K/V pairs and ids of one tile, loaded a tile ahead
+    float2 kr[PAIRS], vr[PAIRS];
+    int jid[PAIRS];
+    auto load_tile = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < PAIRS; ++u) {
+        const int j = j0 + tid / NPR + RPS * u;
+        kr[u] = vr[u] = make_float2(0.f, 0.f);
+        jid[u] = 0;
+        if (j < S) {
+          kr[u] = *reinterpret_cast<const float2*>(kg + size_t(j) * rowk + 2 * spair);
+          vr[u] = *reinterpret_cast<const float2*>(vg + size_t(j) * rowk + 2 * spair);
+          if (MODE != kNope && rot[p]) jid[u] = posb[j];
+        }
+      }
+    };
+    const int jfirst = static_cast<int>(jlo / kBNf) * kBNf;
+    load_tile(jfirst);
+    for (int j0 = jfirst; j0 <= jhi; j0 += kBNf) {
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) {
         const int n = tid / NPR + RPS * u;
-        const int j = j0 + n;
-        float x0 = 0.f, x1 = 0.f, v0 = 0.f, v1 = 0.f;
-        if (j < S) {
-          x0 = kg[size_t(j) * rowk + 2 * spair];
-          x1 = kg[size_t(j) * rowk + 2 * spair + 1];
-          v0 = vg[size_t(j) * rowk + 2 * spair];
-          v1 = vg[size_t(j) * rowk + 2 * spair + 1];
-          if (MODE != kNope && rot[p]) {
-            float s, c;
-            rope_sincos(rot_index_f<MODE>(posb[j], rot[p], a), sflo, sfhi, s, c);
-            float y0, y1;
-            rot_pair(x0, x1, c, s, y0, y1);
-            x0 = y0;
-            x1 = y1;
-          }
+        float x0 = kr[u].x, x1 = kr[u].y;
+        if (MODE != kNope && rot[p] && j0 + n < S) {
+          float s, c;
+          rope_sincos(rot_index_f<MODE>(jid[u], rot[p], a), sflo, sfhi, s, c);
+          float y0, y1;
+          rot_pair(x0, x1, c, s, y0, y1);
+          x0 = y0;
+          x1 = y1;
         }
         Ks[n][2 * spair] = x0;
         Ks[n][2 * spair + 1] = x1;
-        Vs[n][2 * spair] = v0;
-        Vs[n][2 * spair + 1] = v1;
+        Vs[n][2 * spair] = vr[u].x;
+        Vs[n][2 * spair + 1] = vr[u].y;
       }
       __syncthreads();
+      if (j0 + kBNf <= jhi) load_tile(j0 + kBNf);  // in flight during this tile's math
       float sc[kBNf];
       float mx = -INFINITY;
 #pragma unroll
@@ -134,7 +149,8 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < DH; ++c) acc = fmaf(q[c], Ks[n][part * DH + c], acc);
-        if (TPR == 2) acc += __shfl_xor(acc, 1);
+#pragma unroll
+        for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
         const int dist = i - (j0 + n);
         const bool keep = dist >= dlo[p] && dist <= dhi[p];
         sc[n] = keep ? acc * sl2 : -INFINITY;
@@ -168,9 +184,9 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
 
 template <int D, int MODE>
 hipError_t launch_f(const PrefillArgs& a0, hipStream_t stream) {
-  // rows per workgroup = 256 / (D / 64)
+  // rows per workgroup = 256 / (D / 8)
   PrefillArgs a = a0;
-  a.BMp = (kThreadsF / (D / 64)) / a.HG;
+  a.BMp = (kThreadsF / (D / 8)) / a.HG;
   a.n_pblocks = (a.S + a.BMp - 1) / a.BMp;
   const int64_t n = int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks;
   hipLaunchKernelGGL((prefill_fp32_kernel<D, MODE>), dim3(static_cast<unsigned>(n)), dim3(kThreadsF), 0,
