@@ -521,6 +521,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // with the LDS stores of this thread's rows of K tile t+2 and V tile t+1 one
   // per MFMA slot, scheduling barriers keeping that order. Operand reads run
   // one PV step / three QK steps ahead of their MFMAs.
+  // NoPE: the V operands of the first two PV steps (keys 0-31, which this
+  // wave's group staged itself) are read at the start of the vector phase,
+  // which has no rotation work to hide and leaves this wave's LDS port idle
+  // (one wave reads only about a quarter of the CU's LDS rate, so the matrix
+  // phase is bound by its own operand reads). The rotating modes measured
+  // slower with it: their vector phase is already full.
+  constexpr bool kVpre = MODE == kNope;
+  u32x4_t vpre[kVpre ? 2 : 1][DB];
+  auto read_vpre = [&](int t) __attribute__((always_inline)) {
+    const uint16_t* vbase = &Vs[t & 1][vrow0 * VRow + vcol0];
+#pragma unroll
+    for (int kk = 0; kk < (kVpre ? 2 : 0); ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2_t va = lds_read_tr16(vbase + kk * 16 * VRow + db * 32);
+        const u32x2_t vb = lds_read_tr16(vbase + kk * 16 * VRow + 8 * VRow + db * 32);
+        vpre[kk][db] = u32x4_t{va[0], va[1], vb[0], vb[1]};
+      }
+  };
   auto mphase = [&](int t) __attribute__((always_inline)) {
     const int tk = t + 2, tv = t + 1;
     uint16_t* kdst = &Ks[tk & 1][sr * KRow + sc * 8];
@@ -552,18 +571,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       for (int nb = 0; nb < 2; ++nb) dst[nb] = *reinterpret_cast<const u32x4_t*>(kbase + nb * 32 * KRow + ks * 16);
     };
     int pc = 0;  // next staging piece
-    read_v(0, vop[0]);
+    read_v(kVpre ? 2 : 0, vop[0]);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) {
-        read_v(kk + 1, vop[(kk + 1) & 1]);
-      } else {
+      if (kVpre ? kk == 1 : kk + 1 < 4) {
+        read_v(kVpre ? 3 : kk + 1, vop[kVpre ? 1 : (kk + 1) & 1]);
+      } else if (kk == 3) {
 #pragma unroll
         for (int ks = 0; ks < KA; ++ks) read_k(ks, kop[ks]);
       }
+      const u32x4_t* vk = kVpre ? (kk < 2 ? vpre[kk & (kVpre ? 1 : 0)] : vop[(kk - 2) & 1]) : vop[kk & 1];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        oacc[db] = mfma32x32x16(vop[kk & 1][db], pop[kk], oacc[db]);
+        oacc[db] = mfma32x32x16(vk[db], pop[kk], oacc[db]);
         piece(pc++);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -669,6 +689,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       const int srot = pass_of(t + 2) ? rot1 : rot0;
       if (srot != kreg_rot) load_kregs(srot);
     }
+    if (kVpre) read_vpre(t);
     softmax_step(t);  // P of a tile with no kept key is zero
     if (MODE == kBifocal && t + 1 < T && pass_of(t + 1) != pass_of(t)) load_q(pass_of(t + 1));
     lds_barrier();
