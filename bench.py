@@ -167,6 +167,23 @@ def bench_copy(steps, warmup, nbytes=1 << 30):
     return dict(avg_ms=avg, read_bytes=nbytes, write_bytes=nbytes, gbs=2 * nbytes / (avg * 1e-3) / 1e9)
 
 
+def bench_gemm(steps, warmup, n=8192):
+    """Ceiling reference for the MFMA roofline: a large bf16 GEMM through torch
+    (hipBLASLt), 2 n^3 flop per launch. Not part of the measured path."""
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+
+    def step(_):
+        torch.mm(a, b, out=c)
+
+    ms, _ = time_launches(step, steps, warmup)
+    avg = sum(ms) / len(ms)
+    return dict(avg_ms=avg, tflops=2.0 * n ** 3 / (avg * 1e-3) / 1e12)
+
+
 def cpu_baseline(w, inp, n_rows: int):
     """The fp64 oracle, as it stands, on a bounded sample of query rows of the same workload."""
     import numpy as np
@@ -271,6 +288,15 @@ def main():
                            "avg_us": round(d["avg_ms"] * 1e3, 2), "kv_bytes": d["bytes"],
                            "cache_copies": d["copies"]}
             torch.cuda.empty_cache()
+        # what this machine reaches on plain library work, for scale: a bf16 GEMM
+        # (MFMA ceiling in practice) and a 1 GiB streaming copy (HBM ceiling in practice)
+        gm = bench_gemm(20, 3)
+        cp = bench_copy(20, 3)
+        props = torch.cuda.get_device_properties(0)
+        extra["ceilings"] = {"bf16_gemm_8192_tflops": round(gm["tflops"], 1),
+                             "copy_1GiB_gbs": round(cp["gbs"], 1),
+                             "device": props.name, "compute_units": props.multi_processor_count}
+        torch.cuda.empty_cache()
     result["extra"] = extra
     if not args.no_cpu:
         log("cpu baseline (oracle on sampled rows)")

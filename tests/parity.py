@@ -59,16 +59,19 @@ def gpu_prefill(inputs, mode, unfused=False, **kw):
     return o, lse
 
 
-def oracle_prefill(inputs, mode, dtype, rows=None, **kw):
+def oracle_prefill(inputs, mode, dtype, rows=None, operand_round="same", **kw):
+    """Prefill oracle. By default the rotated operands are rounded to the input dtype
+    (the parity contract); operand_round=None gives the exact fp64 result."""
     q, k, v = (to_np(inputs[n]) for n in ("q", "k", "v"))
     pos = inputs["pos"].numpy()
     kw = {("softmax_scale" if k_ == "softmax_scale" else k_): v_ for k_, v_ in kw.items()}
     if kw.get("softmax_scale", 0.0) == 0.0:
         kw.pop("softmax_scale", None)
-    return O.prefill_ref(q, k, v, pos, mode, operand_round=dtype, rows=rows, **kw)
+    rnd = dtype if operand_round == "same" else operand_round
+    return O.prefill_ref(q, k, v, pos, mode, operand_round=rnd, rows=rows, **kw)
 
 
-def check_prefill(inputs, mode, dtype, rows=None, what="", unfused=False, **kw):
+def check_prefill(inputs, mode, dtype, rows=None, what="", unfused=False, report_exact=False, **kw):
     t0 = time.time()
     o, lse = gpu_prefill(inputs, mode, unfused=unfused, **kw)
     t1 = time.time()
@@ -79,6 +82,12 @@ def check_prefill(inputs, mode, dtype, rows=None, what="", unfused=False, **kw):
         o_np = o_np[:, rows]
         lse_np = lse_np[:, :, rows]
     log(f"{what}: gpu {t1 - t0:.2f}s oracle {t2 - t1:.2f}s")
+    if report_exact and dtype == "bf16":
+        # for the record only: the same rows against the oracle with unrounded operands
+        o_ex, lse_ex = oracle_prefill(inputs, mode, dtype, rows=rows, operand_round=None, **kw)
+        mx, mr = errors(o_np, o_ex)
+        log(f"{what}: vs exact-operand oracle (not gated) max_abs={mx:.3e} mean_rel={mr:.3e} "
+            f"lse max_abs={float(np.max(np.abs(lse_np - lse_ex))):.3e}")
     res = assert_close(o_np, o_ref, dtype, what)
     lerr = float(np.max(np.abs(lse_np - lse_ref)))
     log(f"{what}: lse max_abs={lerr:.3e}")
