@@ -447,22 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   };
 
-  // matrix phase, part 1: O^T += V^T P^T for tile t
-  auto pv_step = [&](int t) __attribute__((always_inline)) {
-    const uint16_t* vbase = &Vs[t & 1][vrow0 * VRow + vcol0];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint16_t* vrow = vbase + kk * 16 * VRow;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2_t va = lds_read_tr16(vrow + db * 32);
-        const u32x2_t vb = lds_read_tr16(vrow + 8 * VRow + db * 32);
-        const u32x4_t vop = {va[0], va[1], vb[0], vb[1]};
-        oacc[db] = mfma32x32x16(vop, pop[kk], oacc[db]);
-      }
-    }
-  };
-  // matrix phase, part 2: S^T = K Q^T for tile t
+  // S^T = K Q^T for tile t (prologue only; the main loop uses the matrix phase below)
   auto qk_step = [&](int t) __attribute__((always_inline)) {
     const uint16_t* kbase = &Ks[t & 1][lr * KRow + lg * 8];
 #pragma unroll
@@ -493,7 +478,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // phase of tile t: the rotation index, the exact phase (quarter-rate integer
   // multiplies), sin/cos and the pair rotations are independent of the softmax,
   // so they fill its dependency gaps, and the matrix phase is left with the
-  // LDS stores. The raw rows arrived during the previous matrix phase.
+  // LDS stores. The raw rows were loaded at the end of the previous matrix
+  // phase.
   u32x4_t krot[NU];
   auto rotate_k = [&](int t) __attribute__((always_inline)) {
     if (MODE == kNope) return;
@@ -580,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
         for (int ks = 0; ks < KA; ++ks) read_k(ks, kop[ks]);
       }
-      const u32x4_t* vk = kVpre ? (kk < 2 ? vpre[kk & (kVpre ? 1 : 0)] : vop[(kk - 2) & 1]) : vop[kk & 1];
+      const u32x4_t* vk = (kVpre && kk < 2) ? vpre[kVpre ? kk : 0] : vop[kk & 1];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         oacc[db] = mfma32x32x16(vk[db], pop[kk], oacc[db]);
