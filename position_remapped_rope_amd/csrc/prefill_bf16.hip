@@ -75,6 +75,15 @@ __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t of
 __device__ __forceinline__ int bload_i32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// The same with a wave-uniform part of the offset in the instruction's scalar
+// offset field: per-lane offsets stay loop-invariant, so the main loop forms
+// no vector addresses.
+__device__ __forceinline__ u32x4_t bload16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ int bload_i32s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
 
 // Workgroup barrier that orders LDS accesses only. Unlike __syncthreads() it
 // does not wait for outstanding global loads, so prefetches stay in flight
@@ -208,6 +217,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int sc = gtid % CPR;                 // 16-byte column chunk this thread stages
   const int sr = group * HR + gtid / CPR;    // first row this thread stages (then sr + RPS)
   const uint32_t kcol_b = uint32_t(kvh) * D * 2 + sc * 16;
+  const uint32_t srow_kv = uint32_t(sr) * rowk_b + kcol_b;  // this thread's first staged row, byte offset in K/V
+  const uint32_t srow_id = uint32_t(sr) * 4;                // and in the ids
 
   // Per-chunk constants kept in LDS rather than registers: the 4 pair
   // frequencies of each 16-byte column chunk, and for each rotation kind the
@@ -342,22 +353,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   auto stage_load_nb = [&](int tk, int tv) __attribute__((always_inline)) {
     int p, kt;
     tile_of(tk, p, kt);
-    const uint32_t j0 = uint32_t(kt) * kBN;
+    const uint32_t j0 = uint32_t(kt) * kBN;  // wave-uniform
     // issue order = use order (ids, K rows, V rows), so each use waits only for
     // its own loads
     if (MODE != kNope) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) kid[u] = bload_i32(pres, (j0 + sr + RPS * u) * 4);
+      for (int u = 0; u < NU; ++u) kid[u] = bload_i32s(pres, srow_id + RPS * 4 * u, j0 * 4);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) kraw[u] = bload16(kres, (j0 + sr + RPS * u) * rowk_b + kcol_b);
+    for (int u = 0; u < NU; ++u) kraw[u] = bload16s(kres, srow_kv + RPS * rowk_b * u, j0 * rowk_b);
     __builtin_amdgcn_sched_barrier(0);
     int pv, ktv;
     tile_of(tv, pv, ktv);
     const uint32_t jv = uint32_t(ktv) * kBN;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) vraw[u] = bload16(vres, (jv + sr + RPS * u) * rowk_b + kcol_b);
+    for (int u = 0; u < NU; ++u) vraw[u] = bload16s(vres, srow_kv + RPS * rowk_b * u, jv * rowk_b);
   };
   auto fix_row1 = [&](int tk) __attribute__((always_inline)) {
     if (MODE != kNope && NU > 1 && need_fix) {
