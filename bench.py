@@ -167,6 +167,25 @@ def bench_copy(steps, warmup, nbytes=1 << 30):
     return dict(avg_ms=avg, read_bytes=nbytes, write_bytes=nbytes, gbs=2 * nbytes / (avg * 1e-3) / 1e9)
 
 
+def bench_rope_apply(steps, warmup, S=131072, H=8, d=128):
+    """prope_rope_apply on a 128K-token, 8-head bf16 K tensor (the base-rotated
+    cache of the decode workload), out of place: bytes = read x + write y."""
+    import torch
+    import position_remapped_rope_amd as P
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    x = torch.randn(1, S, H, d, device="cuda:0", generator=g).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    pos = torch.arange(S, dtype=torch.int32, device="cuda:0").reshape(1, S)
+
+    def step(_):
+        P.rope_apply(x, pos, 1e6, out=y)
+
+    ms, _ = time_launches(step, steps, warmup)
+    avg = sum(ms) / len(ms)
+    nbytes = 2 * x.numel() * x.element_size()
+    return dict(avg_ms=avg, bytes=nbytes, gbs=nbytes / (avg * 1e-3) / 1e9)
+
+
 def bench_gemm(steps, warmup, n=8192):
     """Ceiling reference for the MFMA roofline: a large bf16 GEMM through torch
     (hipBLASLt), 2 n^3 flop per launch. Not part of the measured path."""
@@ -288,6 +307,9 @@ def main():
                            "avg_us": round(d["avg_ms"] * 1e3, 2), "kv_bytes": d["bytes"],
                            "cache_copies": d["copies"]}
             torch.cuda.empty_cache()
+        ra = bench_rope_apply(20, 3)
+        extra["rope_apply_128k_k"] = {"gbs": round(ra["gbs"], 1), "frac_hbm_peak": round(ra["gbs"] / PEAK_HBM_GBS, 4),
+                                      "avg_us": round(ra["avg_ms"] * 1e3, 2), "bytes": ra["bytes"]}
         # what this machine reaches on plain library work, for scale: a bf16 GEMM
         # (MFMA ceiling in practice) and a 1 GiB streaming copy (HBM ceiling in practice)
         gm = bench_gemm(20, 3)
