@@ -157,6 +157,8 @@ def _softmax_rows(scores: np.ndarray, keep: np.ndarray, vals: np.ndarray):
     Rows with no kept key give O = 0 and lse = -inf.
     """
     s = np.where(keep, scores, -np.inf)
+    if s.shape[-1] == 0:  # no key at all (an empty sequence)
+        return np.zeros((s.shape[0], vals.shape[-1])), np.full(s.shape[0], -np.inf)
     m = np.max(s, axis=-1, keepdims=True)
     empty = ~np.isfinite(m)
     m = np.where(empty, 0.0, m)

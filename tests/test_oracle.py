@@ -431,6 +431,23 @@ def test_decode_ragged_kv_len():
     assert np.allclose(o[1], v[1, 0][np.arange(Hq) // 1], atol=1e-14)
 
 
+def test_decode_empty_sequence():
+    """kv_len 0 (an empty slot in a batch): no key, so O = 0 and LSE = -inf, and the
+    other sequences' results are what they are alone."""
+    B, L, Hq, Hkv, d = 3, 20, 4, 2, 8
+    q, k, v = _rand_qkv(B, L, Hq, Hkv, d, 27)
+    lens = [0, 13, 0]
+    o, l = O.decode_ref(q[:, 0], k, v, lens, "bifocal", rope_base=1e4, remap_scale=2, window_left=3)
+    assert np.all(o[0] == 0) and np.all(o[2] == 0)
+    assert np.all(np.isneginf(l[0])) and np.all(np.isneginf(l[2]))
+    o1, l1 = O.decode_ref(q[1:2, 0], k[1:2, :13], v[1:2, :13], [13], "bifocal",
+                          rope_base=1e4, remap_scale=2, window_left=3)
+    assert np.allclose(o[1], o1[0], atol=1e-14) and np.allclose(l[1], l1[0], atol=1e-14)
+    # nope/rope go through the same masked softmax
+    o, l = O.decode_ref(q[:, 0], k, v, lens, "nope", window_left=5)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[2])) and np.all(np.isfinite(l[1]))
+
+
 def test_operand_rounding_identity_on_bf16_inputs():
     rng = _rng(27)
     q = O.round_to_bf16(rng.standard_normal((1, 20, 2, 8)))
