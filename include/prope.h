@@ -141,8 +141,10 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
  *     kv_len[b]-1 (the base view, Jet-Long Eq. (6)'s q_local).
  *   k_cache, v_cache [B,Lmax,Hkv,d]: keys rotated at their own index (Jet-Long
  *     Eq. (4)); the cache is never modified.
- *   kv_len [B] int32 device array, 1 <= kv_len[b] <= Lmax, counting the new
- *     token (its key is at index kv_len[b]-1).
+ *   kv_len [B] int32 device array, 0 <= kv_len[b] <= Lmax, counting the new
+ *     token (its key is at index kv_len[b]-1). kv_len[b] = 0 is an empty slot:
+ *     its O rows are 0 and its LSE is -inf (no key to attend to). A value
+ *     outside [0, Lmax] is clamped to that range, so no read leaves the cache.
  *   o [B,Hq,d] dtype `dt`; lse [B,Hq] float32, may be NULL.
  *   BIFOCAL: keys with (kv_len-1) - j <= w0 score q.k; farther keys score
  *     RoPE(q, dq).RoPE(k_j, dk_j) with dq = floor(p_q/s) - p_q and

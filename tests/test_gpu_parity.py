@@ -271,6 +271,27 @@ def test_decode_small(name, shape, mode, kw, lens):
     assert float(np.max(np.abs(lse.cpu().numpy() - lse_ref))) < LSE_TOL["bf16"]
 
 
+@pytest.mark.parametrize("mode,kw", [
+    ("bifocal", dict(rope_base=1e6, remap_scale=4, window_left=300)),
+    ("nope", dict(window_left=100)),
+])
+def test_decode_empty_sequences(mode, kw):
+    """Empty slots (kv_len 0) in a batch give O = 0 and LSE = -inf; the other
+    sequences match the oracle."""
+    B, L, Hq, Hkv, d = 4, 3000, 8, 2, 128
+    w = W.Workload("t", "decode", B=B, S=L, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", mode=mode,
+                   rope_base=kw.get("rope_base", 1e4), seed=515)
+    inp = W.make_decode_inputs(w)
+    inp["kv_len"] = torch.tensor([0, 3000, 0, 1], dtype=torch.int32)
+    o, lse = gpu_decode(inp, mode=mode, **kw)
+    o_ref, lse_ref = oracle_decode(inp, mode, **kw)
+    o, lse = to_np(o), lse.cpu().numpy()
+    for b in (0, 2):
+        assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b])), b
+    assert_close(o[[1, 3]], o_ref[[1, 3]], "bf16", f"{mode} with empty slots")
+    assert float(np.max(np.abs(lse[[1, 3]] - lse_ref[[1, 3]]))) < LSE_TOL["bf16"]
+
+
 def test_decode_workspace_reuse():
     """One workspace serves consecutive calls with other lengths: each result is
     bit-identical to a call with a fresh workspace (no state survives a call)."""
