@@ -110,6 +110,27 @@ int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, flo
                        const prope_params* params, void* stream);
 
 /*
+ * Prefill as prope_attn_prefill (same operation, arguments, checks and
+ * results, bit for bit), scheduled through a work queue: one workgroup per
+ * compute unit takes (row block, head group) items from eight queues, one per
+ * XCD, heaviest row block first, and takes items left in the other XCDs'
+ * queues when its own is empty. The XCDs of one device can run at different
+ * speeds, and a fixed split of the work over them leaves the fast ones idle
+ * at the end; the queue removes that tail.
+ *   queue: caller-owned device buffer of prope_prefill_queue_size() bytes,
+ *     128-byte aligned, all zero before its first use (e.g. a zero-filled
+ *     allocation). Every call leaves it zero again, so it can be reused by the
+ *     calls that follow on the same stream. Calls that may run at the same
+ *     time (other streams, graph replays) need distinct buffers. NULL or
+ *     misaligned -> PROPE_ERR_INVALID_ARG.
+ *   fp32 (dt = PROPE_FP32) runs the static schedule and does not touch queue.
+ */
+size_t prope_prefill_queue_size(void);
+int prope_attn_prefill_queued(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int dt,
+                              const prope_params* params, void* queue, void* stream);
+
+/*
  * Bifocal prefill composed as the pages' unfused construction (Jet-Long
  * "Efficient Long-Context Extension with Dynamic Bifocal RoPE", section 3.3,
  * Eq. (7)): three ordinary attention calls, each returning O_X and its LSE,
@@ -125,9 +146,10 @@ int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, flo
  *   pos is required (ids >= 0).
  *   workspace: caller-owned device buffer, 256-byte aligned, of at least
  *     prope_bifocal_unfused_workspace_size(B, S, Hq, d, dt) bytes (O_A, O_C,
- *     three LSE vectors, remote ids); too small -> PROPE_ERR_WORKSPACE. Its
+ *     three LSE vectors, remote ids, and the work queue of the three calls,
+ *     as in prope_attn_prefill_queued); too small -> PROPE_ERR_WORKSPACE. Its
  *     contents need no initialisation and are scratch after the call.
- *   Enqueues five kernels on `stream`.
+ *   Enqueues six kernels on `stream` (five for fp32, which has no queue).
  */
 size_t prope_bifocal_unfused_workspace_size(int B, int S, int Hq, int d, int dt);
 int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void* v, void* o, float* lse,

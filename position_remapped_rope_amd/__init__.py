@@ -11,7 +11,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["NOPE", "ROPE", "BIFOCAL", "PropeError", "lib", "lib_path", "rope_apply", "prefill",
+__all__ = ["NOPE", "ROPE", "BIFOCAL", "PropeError", "lib", "lib_path", "rope_apply", "prefill", "prefill_queue",
            "prefill_bifocal_unfused", "bifocal_unfused_workspace_size", "decode", "decode_workspace_size",
            "group_size", "status_string", "EXPORTED_SYMBOLS"]
 
@@ -21,7 +21,8 @@ REMOTE_ALIAS, REMOTE_INTERP = 0, 1
 _REMOTE = {"alias": REMOTE_ALIAS, "interp": REMOTE_INTERP}
 BF16, FP32 = 0, 1
 
-EXPORTED_SYMBOLS = ("prope_attn_prefill", "prope_attn_prefill_bifocal_unfused",
+EXPORTED_SYMBOLS = ("prope_attn_prefill", "prope_attn_prefill_queued", "prope_prefill_queue_size",
+                    "prope_attn_prefill_bifocal_unfused",
                     "prope_bifocal_unfused_workspace_size", "prope_attn_decode", "prope_decode_workspace_size",
                     "prope_rope_apply", "prope_group_size", "prope_status_string", "prope_version")
 
@@ -59,6 +60,11 @@ def lib():
     L.prope_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      ctypes.POINTER(PropeParams), vp]
     L.prope_attn_prefill.restype = i32
+    L.prope_attn_prefill_queued.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(PropeParams), vp, vp]
+    L.prope_attn_prefill_queued.restype = i32
+    L.prope_prefill_queue_size.argtypes = []
+    L.prope_prefill_queue_size.restype = ctypes.c_size_t
     L.prope_attn_prefill_bifocal_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                                      ctypes.POINTER(PropeParams), vp, ctypes.c_size_t, vp]
     L.prope_attn_prefill_bifocal_unfused.restype = i32
@@ -125,6 +131,22 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+# Work-queue buffers of the queued prefill, one per (device, stream): calls on
+# one stream run in order and each leaves its queue zero for the next.
+_queues = {}
+
+
+def prefill_queue(device, stream: int):
+    """The zero-filled work-queue buffer of prope_attn_prefill_queued for this (device, stream)."""
+    import torch
+    key = (torch.device(device).index, int(stream))
+    buf = _queues.get(key)
+    if buf is None:
+        buf = torch.zeros(int(lib().prope_prefill_queue_size()), dtype=torch.uint8, device=device)
+        _queues[key] = buf
+    return buf
+
+
 def group_size(L: int, w_pretrained: int) -> int:
     return lib().prope_group_size(int(L), int(w_pretrained))
 
@@ -150,10 +172,13 @@ def rope_apply(x, pos, rope_base: float, out=None):
 
 def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
             remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
-            out=None, lse=None, return_lse: bool = False, w_pretrained: int = 0, remote_map="alias"):
+            out=None, lse=None, return_lse: bool = False, w_pretrained: int = 0, remote_map="alias",
+            schedule: str = "queue"):
     """Causal attention with RoPE fused under remapped ids (see include/prope.h).
 
     q [B,S,Hq,d], k/v [B,S,Hkv,d] unrotated; pos int32 [B,S] (None for NoPE).
+    schedule "queue" calls prope_attn_prefill_queued with this stream's queue
+    buffer, "static" calls prope_attn_prefill; both give the same bits.
     Returns O [B,S,Hq,d] (and LSE float32 [B,Hq,S] if return_lse).
     """
     import torch
@@ -170,8 +195,15 @@ def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained, remote_map)
-    _check(L.prope_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos),
-                                B, S, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p), _stream(q)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos), B, S, Hq, Hkv, d, _dtype_code(q),
+            ctypes.byref(p))
+    st = _stream(q)
+    if schedule == "queue":
+        _check(L.prope_attn_prefill_queued(*args, _ptr(prefill_queue(q.device, st)), st))
+    elif schedule == "static":
+        _check(L.prope_attn_prefill(*args, st))
+    else:
+        raise PropeError(f"schedule must be 'queue' or 'static', not {schedule!r}")
     return (o, lse) if return_lse else o
 
 

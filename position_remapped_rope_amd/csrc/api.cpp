@@ -82,9 +82,20 @@ int check_prefill(const void* q, const void* k, const void* v, const void* o, co
   return PROPE_OK;
 }
 
+// compute units of the current device (256 if it cannot be read)
+int device_cus() {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    n_cu = 256;
+  return n_cu;
+}
+
 PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* pos,
-                         int B, int S, int Hq, int Hkv, int d, const prope_params& p) {
+                         int B, int S, int Hq, int Hkv, int d, const prope_params& p, uint32_t* queue = nullptr) {
   PrefillArgs a{};
+  a.queue = queue;
+  a.n_cu = queue ? device_cus() : 0;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.pos = pos;
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.D = d;
   a.G = Hq / Hkv;
@@ -115,10 +126,10 @@ int run_prefill(const PrefillArgs& a, int dt, void* stream) {
 }
 
 // Workspace of the unfused composition: O_A and O_C in the input dtype, the
-// three LSE vectors and the remote ids, each region 256-byte aligned. O_B is
-// written into the caller's output.
+// three LSE vectors, the remote ids and the work queue of the three calls,
+// each region 256-byte aligned. O_B is written into the caller's output.
 struct UnfusedLayout {
-  size_t oa, oc, la, lb, lc, ids, total;
+  size_t oa, oc, la, lb, lc, ids, queue, total;
 };
 UnfusedLayout unfused_layout(int B, int S, int Hq, int d, int dt) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -131,7 +142,8 @@ UnfusedLayout unfused_layout(int B, int S, int Hq, int d, int dt) {
   l.lb = l.la + lbytes;
   l.lc = l.lb + lbytes;
   l.ids = l.lc + lbytes;
-  l.total = l.ids + up(size_t(B) * S * sizeof(int32_t));
+  l.queue = l.ids + up(size_t(B) * S * sizeof(int32_t));
+  l.total = l.queue + up(kQueueWords * sizeof(uint32_t));
   return l;
 }
 
@@ -188,6 +200,20 @@ int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, flo
   return run_prefill(a, dt, stream);
 }
 
+size_t prope_prefill_queue_size(void) { return kQueueWords * sizeof(uint32_t); }
+
+int prope_attn_prefill_queued(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int32_t* pos, int B, int S, int Hq, int Hkv, int d, int dt,
+                              const prope_params* params, void* queue, void* stream) {
+  const int pc = check_prefill(q, k, v, o, pos, B, S, Hq, Hkv, d, dt, params);
+  if (pc != PROPE_OK) return pc;
+  if (!queue || reinterpret_cast<uintptr_t>(queue) % 128) return PROPE_ERR_INVALID_ARG;
+  // the fp32 kernel has no queue: it runs its static schedule and leaves the buffer as it is
+  uint32_t* wq = dt == PROPE_BF16 ? static_cast<uint32_t*>(queue) : nullptr;
+  const PrefillArgs a = prefill_args(q, k, v, o, lse, pos, B, S, Hq, Hkv, d, *params, wq);
+  return run_prefill(a, dt, stream);
+}
+
 size_t prope_bifocal_unfused_workspace_size(int B, int S, int Hq, int d, int dt) {
   if (B < 1 || S < 1 || Hq < 1 || d < 1 || (dt != PROPE_BF16 && dt != PROPE_FP32)) return 0;
   return unfused_layout(B, S, Hq, d, dt).total;
@@ -211,6 +237,8 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
   float* lb = reinterpret_cast<float*>(ws + ly.lb);
   float* lc = reinterpret_cast<float*>(ws + ly.lc);
   int32_t* rid = reinterpret_cast<int32_t*>(ws + ly.ids);
+  // the work queue of the three calls: cleared once here, each call leaves it clear
+  uint32_t* wq = dt == PROPE_BF16 ? reinterpret_cast<uint32_t*>(ws + ly.queue) : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int w0 = params->window_left;
 
@@ -223,17 +251,18 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
   if (launch_remap_ids(pos, rid, int64_t(B) * S, make_fastdiv(static_cast<uint32_t>(remote_scale(*params, S))),
                        st) != hipSuccess)
     return PROPE_ERR_HIP;
+  if (wq && launch_zero_words(wq, kQueueWords, st) != hipSuccess) return PROPE_ERR_HIP;
   // B: full causal attention at the remote ids, written straight into o
   call.window_left = -1;
-  int rc = run_prefill(prefill_args(q, k, v, o, lb, rid, B, S, Hq, Hkv, d, call), dt, stream);
+  int rc = run_prefill(prefill_args(q, k, v, o, lb, rid, B, S, Hq, Hkv, d, call, wq), dt, stream);
   if (rc != PROPE_OK) return rc;
   const bool windows = w0 >= 0;  // w0 = -1: no local window, the result is B alone
   if (windows) {
     // A: the local window at the ids themselves; C: the local window at the remote ids
     call.window_left = w0;
-    rc = run_prefill(prefill_args(q, k, v, oa, la, pos, B, S, Hq, Hkv, d, call), dt, stream);
+    rc = run_prefill(prefill_args(q, k, v, oa, la, pos, B, S, Hq, Hkv, d, call, wq), dt, stream);
     if (rc != PROPE_OK) return rc;
-    rc = run_prefill(prefill_args(q, k, v, oc, lc, rid, B, S, Hq, Hkv, d, call), dt, stream);
+    rc = run_prefill(prefill_args(q, k, v, oc, lc, rid, B, S, Hq, Hkv, d, call, wq), dt, stream);
     if (rc != PROPE_OK) return rc;
   }
   return launch_eq7_merge(oa, la, o, lb, oc, lc, lse, B, S, Hq, d, dt, windows, st) == hipSuccess ? PROPE_OK
@@ -272,10 +301,7 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_len = kv_len;
   a.ws = static_cast<float*>(workspace);
   a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv; a.D = d; a.G = Hq / Hkv;
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
-    n_cu = 256;
+  const int n_cu = device_cus();
   const int64_t wg_large = int64_t(B) * Hkv * ((Lmax + kDecodeChunkLarge - 1) / kDecodeChunkLarge);
   a.chunk = wg_large <= n_cu ? kDecodeChunkLarge : kDecodeChunk;
   a.n_chunks = (Lmax + a.chunk - 1) / a.chunk;

@@ -25,6 +25,12 @@ __global__ __launch_bounds__(256) void remap_ids_kernel(const int32_t* __restric
   if (i < n) out[i] = static_cast<int32_t>(fastdiv(static_cast<uint32_t>(pos[i]), s));
 }
 
+// clears the prefill work queue that the three calls share (vector stores)
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = int(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 // 8 output elements per thread (bf16: one 16-byte vector; fp32: two).
 template <typename T>
 struct Vec8 {
@@ -110,6 +116,11 @@ __global__ __launch_bounds__(256) void eq7_merge_kernel(const T* __restrict__ oa
 hipError_t launch_remap_ids(const int32_t* pos, int32_t* out, int64_t n, const FastDiv& s, hipStream_t stream) {
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(remap_ids_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, pos, out, n, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 

@@ -32,7 +32,15 @@ struct PrefillArgs {
   float scale_log2;   // softmax scale * log2(e)
   RopeFreq f;         // theta_i at the base ids
   RopeFreq fr;        // theta_i at the remote ids: theta_i (alias) or theta_i / s
+  uint32_t* queue;    // bf16: work-queue counters (kQueueWords), or nullptr: one item per workgroup
+  int n_cu;           // compute units of the device (persistent grid size with a queue)
 };
+
+// Prefill work queue: 8 per-XCD item counters, 8 per-XCD done counts and one
+// global done count, each in its own 128-byte line (atomics on one line
+// serialise).
+constexpr int kQueueLine = 32;  // 32-bit words per counter line
+constexpr int kQueueWords = 17 * kQueueLine;
 
 struct DecodeArgs {
   const void* q;
@@ -72,6 +80,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_fp32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_remap_ids(const int32_t* pos, int32_t* out, int64_t n, const FastDiv& s, hipStream_t stream);
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream);
 hipError_t launch_eq7_merge(const void* oa, const float* la, void* o, const float* lb, const void* oc,
                             const float* lc, float* lse, int B, int S, int Hq, int d, int dt, bool windows,
                             hipStream_t stream);

@@ -152,8 +152,80 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int lr = lane & 31, lg = lane >> 5;
   const int group = wave >> 2;  // waves w and w + 4 share a SIMD
 
-  // ---- work item --------------------------------------------------------
-  int item = xcd_remap(blockIdx.x, gridDim.x);
+  // ---- work items ---------------------------------------------------------
+  // An item is (sequence, KV head, head subgroup, row block). Without a queue
+  // every workgroup runs the one item blockIdx names. With a queue the grid is
+  // persistent and items come from 8 queues, one per XCD (blockIdx % 8 is the
+  // XCD a workgroup runs on): queue x holds the x-th contiguous eighth of the
+  // items (whole head groups when possible, so its K/V tiles stay in that XCD's
+  // L2), handed out heaviest row block first. A workgroup whose own queue is
+  // empty takes items from the others. The XCDs run at different speeds, so a
+  // fixed split of the items over them leaves the fast ones idle at the end.
+  const int n_items = a.B * a.Hkv * a.n_hsub * a.n_pblocks;
+  const int q8 = n_items / 8, r8 = n_items % 8;
+  auto q_start = [&](int x) { return x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8; };
+  auto q_len = [&](int x) { return q8 + (x < r8 ? 1 : 0); };
+  // item of the k-th claim on queue x: a queue made of whole head groups goes
+  // row block major across its groups, heaviest (last) row block first
+  auto q_item = [&](int x, int k) {
+    const int st = q_start(x), len = q_len(x), npb = a.n_pblocks;
+    if (st % npb == 0 && len % npb == 0) {
+      const int ng = len / npb;
+      return st + (k % ng) * npb + k / ng;
+    }
+    return st + k;
+  };
+  const int home = blockIdx.x & 7;
+  // each queue's first claims are static (rank blockIdx / 8 among the
+  // workgroups of that XCD); its counter counts the claims after those
+  auto q_static = [&](int x) { return int(gridDim.x) / 8 + (x < int(gridDim.x) % 8 ? 1 : 0); };
+  uint32_t* const wq = a.queue;
+  bool first = true;
+  auto next_item = [&]() -> int {  // run by wave 0; the result is valid in every lane
+    if (first) {
+      first = false;
+      if (!wq) return xcd_remap(blockIdx.x, gridDim.x);
+      const int k0 = int(blockIdx.x) / 8;
+      if (k0 < q_len(home)) return q_item(home, k0);
+    }
+    if (!wq) return -1;
+    int r = -1;
+    if (lane == 0) {
+      const uint32_t k = atomicAdd(&wq[kQueueLine * home], 1u) + q_static(home);
+      if (k < uint32_t(q_len(home))) r = q_item(home, int(k));
+    }
+    r = __shfl(r, 0);
+    if (r >= 0) return r;
+    // own queue empty: read the other queues' counters in one round, then claim
+    // from those that still hold items
+    const int x = (home + lane) & 7;
+    bool has = false;
+    if (lane >= 1 && lane < 8)
+      has = __hip_atomic_load(&wq[kQueueLine * x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + q_static(x) <
+            uint32_t(q_len(x));
+    uint64_t m = __ballot(has);
+    while (m) {
+      const int xs = (home + __builtin_ctzll(m)) & 7;
+      m &= m - 1;
+      if (lane == 0) {
+        const uint32_t k = atomicAdd(&wq[kQueueLine * xs], 1u) + q_static(xs);
+        if (k < uint32_t(q_len(xs))) r = q_item(xs, int(k));
+      }
+      r = __shfl(r, 0);
+      if (r >= 0) return r;
+    }
+    return -1;
+  };
+  __shared__ int s_item;
+#pragma clang loop unroll(disable)
+  for (;;) {
+  if (wave == 0) {
+    const int r = next_item();
+    if (lane == 0) s_item = r;
+  }
+  __syncthreads();
+  int item = s_item;
+  if (item < 0) break;
   const int pb = a.n_pblocks - 1 - (item % a.n_pblocks);  // heavy (late) rows first
   item /= a.n_pblocks;
   const int hsub = item % a.n_hsub;
@@ -725,12 +797,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       a.lse[(size_t(b) * a.Hq + h) * S + i] = lse;
     }
   }
+  __syncthreads();  // LDS and s_item are reused by the next item
+  }  // items
+
+  // Queue clean-up: each workgroup counts itself done on its XCD's counter, the
+  // last of each XCD on the global one, and the very last puts every counter
+  // back to 0, so the buffer is ready for the next launch.
+  if (wq && wave == 0) {
+    uint32_t last = 0;
+    if (lane == 0) {
+      const uint32_t dn = atomicAdd(&wq[kQueueLine * (8 + home)], 1u);
+      if (dn == uint32_t(q_static(home)) - 1)
+        last = atomicAdd(&wq[kQueueLine * 16], 1u) == uint32_t(min(8, int(gridDim.x))) - 1;
+    }
+    last = __shfl(last, 0);
+    if (last && lane < 17) atomicExch(&wq[kQueueLine * lane], 0u);
+  }
 }
 
 template <int D, int MODE>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+  // one workgroup per item, or with a queue one per compute unit (a workgroup
+  // fills a CU: 8 waves at 2 per SIMD)
   const int64_t n = int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3(static_cast<unsigned>(n)), dim3(kThreads), 0,
+  const int64_t grid = a.queue ? (n < a.n_cu ? n : a.n_cu) : n;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
 }

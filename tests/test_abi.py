@@ -141,8 +141,29 @@ def test_unfused_workspace_size_formula():
     for B, S, Hq, d, dt in [(1, 1000, 4, 64, 0), (2, 65536, 32, 128, 0), (1, 77, 3, 128, 1)]:
         ob = up(B * S * Hq * d * (2 if dt == 0 else 4))
         lb = up(B * Hq * S * 4)
-        assert L.prope_bifocal_unfused_workspace_size(B, S, Hq, d, dt) == 2 * ob + 3 * lb + up(B * S * 4)
+        queue = up(17 * 128)  # the three calls' work queue (fp32 leaves it unused)
+        assert L.prope_bifocal_unfused_workspace_size(B, S, Hq, d, dt) == 2 * ob + 3 * lb + up(B * S * 4) + queue
     assert L.prope_bifocal_unfused_workspace_size(0, 10, 4, 64, 0) == 0
+
+
+def _prefill_queued(queue=FAKE + (1 << 20), **kw):
+    L = P.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos=FAKE, B=1, S=16, Hq=4, Hkv=2, d=128, dt=0)
+    a.update(kw)
+    p = _params()
+    return L.prope_attn_prefill_queued(a["q"], a["k"], a["v"], a["o"], a["lse"], a["pos"], a["B"], a["S"], a["Hq"],
+                                       a["Hkv"], a["d"], a["dt"], ctypes.byref(p), queue, None)
+
+
+def test_prefill_queue_size():
+    # 8 per-XCD item counters, 8 per-XCD done counts, 1 global done count, one 128-byte line each
+    assert P.lib().prope_prefill_queue_size() == 17 * 128
+
+
+@pytest.mark.parametrize("kw", [dict(queue=None), dict(queue=FAKE + (1 << 20) + 64), dict(S=0), dict(d=96),
+                                dict(q=None), dict(Hq=6, Hkv=4)])
+def test_prefill_queued_rejects(kw):
+    assert _prefill_queued(**kw) == INVALID
 
 
 def test_workspace_size_formula():

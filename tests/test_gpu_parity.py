@@ -94,6 +94,77 @@ def test_prefill_small(name, shape, mode, kw, ids):
     check_prefill(inp, mode, dtype, what=name, **kw)
 
 
+# Work-queue schedule: the same items as the static one, so the same bits.
+# Items = B * Hkv * (G / HG) * ceil(S / (256 / HG)), HG = 4, 2 or 1 dividing G.
+QUEUED = [
+    # fewer items (5) than XCD queues
+    ("five_items", (1, 300, 4, 1, 128), "bifocal", dict(rope_base=1e6, remap_scale=2, window_left=40)),
+    # 72 items: queues of 9 that split head groups (claims in item order)
+    ("split_groups", (3, 1000, 6, 2, 64), "rope", dict(rope_base=1e4, period=64, window_left=200)),
+    # 512 items, more than the compute units: queues of two whole head groups each
+    ("more_items_than_cus", (2, 8192, 8, 8, 128), "nope", {}),
+    # 1024 items, bifocal with GQA 4
+    ("bifocal_gqa4_1024_items", (1, 16384, 16, 4, 128), "bifocal", dict(rope_base=1e6, remap_scale=4, window_left=1000)),
+]
+
+
+@pytest.mark.parametrize("name,shape,mode,kw", QUEUED, ids=[c[0] for c in QUEUED])
+def test_queued_schedule_equals_static(name, shape, mode, kw):
+    B, S, Hq, Hkv, d = shape
+    inp = _inputs(B, S, Hq, Hkv, d, "bf16", seed=zlib.crc32(name.encode()) % 1000)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    pos = inp["pos"].to(dev) if mode != "nope" else None
+    o_s, l_s = P.prefill(q, k, v, pos, mode=mode, return_lse=True, schedule="static", **kw)
+    queue = P.prefill_queue(dev, torch.cuda.current_stream(dev).cuda_stream)
+    for rep in range(2):  # the second call reuses the buffer the first left zero
+        o_q, l_q = P.prefill(q, k, v, pos, mode=mode, return_lse=True, schedule="queue", **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o_q, o_s) and torch.equal(l_q, l_s), (name, rep)
+        assert int(queue.count_nonzero()) == 0, (name, rep)
+    log(f"{name}: queued == static, queue left zero")
+
+
+def test_queued_schedule_two_streams():
+    """Two streams, each with its own queue buffer, running at the same time."""
+    dev = torch.device("cuda:0")
+    cases = []
+    for i, (S, mode, kw) in enumerate([(12288, "bifocal", dict(rope_base=1e6, remap_scale=3, window_left=2000)),
+                                       (12288, "nope", {})]):
+        inp = _inputs(1, S, 8, 2, 128, "bf16", seed=700 + i)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        pos = inp["pos"].to(dev) if mode != "nope" else None
+        ref = P.prefill(q, k, v, pos, mode=mode, schedule="static", **kw)
+        cases.append((q, k, v, pos, mode, kw, ref))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in cases]
+    outs = []
+    for st, (q, k, v, pos, mode, kw, _) in zip(streams, cases):
+        with torch.cuda.stream(st):
+            outs.append([P.prefill(q, k, v, pos, mode=mode, schedule="queue", **kw) for _ in range(3)])
+    torch.cuda.synchronize()
+    for st, got, case in zip(streams, outs, cases):
+        for o in got:
+            assert torch.equal(o, case[-1])
+        assert int(P.prefill_queue(dev, st.cuda_stream).count_nonzero()) == 0
+
+
+def test_queued_fp32_runs_static_and_leaves_queue():
+    inp = _inputs(1, 150, 4, 2, 64, "fp32", seed=17)
+    dev = torch.device("cuda:0")
+    q, k, v, pos = (inp[n].to(dev) for n in ("q", "k", "v", "pos"))
+    kw = dict(rope_base=1e6, remap_scale=2, window_left=20)
+    queue = P.prefill_queue(dev, torch.cuda.current_stream(dev).cuda_stream)
+    queue.fill_(7)
+    o_q = P.prefill(q, k, v, pos, mode="bifocal", schedule="queue", **kw)
+    o_s = P.prefill(q, k, v, pos, mode="bifocal", schedule="static", **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_q, o_s)
+    assert bool((queue == 7).all())
+    queue.zero_()
+    torch.cuda.synchronize()
+
+
 def test_prefill_period_equals_prereduced_ids():
     inp = _inputs(1, 300, 4, 4, 128, "bf16", seed=9)
     o1 = P.prefill(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), inp["pos"].cuda(), mode="rope",
