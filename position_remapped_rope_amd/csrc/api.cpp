@@ -271,7 +271,7 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
 
 size_t prope_decode_workspace_size(int B, int Lmax, int Hq, int d) {
   if (B < 1 || Lmax < 1 || Hq < 1 || d < 1) return 0;
-  const size_t n_chunks = (size_t(Lmax) + kDecodeChunk - 1) / kDecodeChunk;
+  const size_t n_chunks = (size_t(Lmax) + kDecodeChunkRows - 1) / kDecodeChunkRows;
   return size_t(B) * Hq * n_chunks * (size_t(d) + 2) * sizeof(float);
 }
 
@@ -302,8 +302,15 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
   a.ws = static_cast<float*>(workspace);
   a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv; a.D = d; a.G = Hq / Hkv;
   const int n_cu = device_cus();
+  const int64_t wg_rows = int64_t(B) * (Hkv / 4) * ((Lmax + kDecodeChunkRows - 1) / kDecodeChunkRows);
   const int64_t wg_large = int64_t(B) * Hkv * ((Lmax + kDecodeChunkLarge - 1) / kDecodeChunkLarge);
-  a.chunk = wg_large <= n_cu ? kDecodeChunkLarge : kDecodeChunk;
+  if (Hkv % 4 == 0 && wg_rows <= n_cu) {
+    a.hpw = 4;
+    a.chunk = kDecodeChunkRows;
+  } else {
+    a.hpw = 1;
+    a.chunk = wg_large <= n_cu ? kDecodeChunkLarge : kDecodeChunk;
+  }
   a.n_chunks = (Lmax + a.chunk - 1) / a.chunk;
   a.mode = params->mode;
   a.window_left = params->window_left;

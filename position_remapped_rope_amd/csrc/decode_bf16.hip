@@ -10,9 +10,12 @@
 // registers from exact integer phases; nothing is written back. NOPE/ROPE caches already carry their rotation, so those modes
 // score q . k_j with an optional window.
 //
-// Kernel 1 (split): one workgroup per (chunk of a.chunk keys, KV head,
-// sequence); each of its 4 waves streams a quarter of the chunk in steps of 32
-// keys with no workgroup barrier. Per step and wave:
+// Kernel 1 (split): one workgroup per (chunk of a.chunk keys, group of a.hpw
+// KV heads, sequence). With hpw = 4 each of its 4 waves streams the whole chunk
+// of one head (the 4 heads' slices of a key row are contiguous); with hpw = 1
+// the 4 waves stream a quarter of the chunk of one head each and merge their
+// partials in LDS at the end. Waves step through their keys 32 at a time with
+// no workgroup barrier. Per step and wave:
 //   - K rows are loaded straight into the A-operand layout of
 //     v_mfma_f32_16x16x32_bf16 (lane l: key l%16, dims 8*(l/16) + 32*ks ..+7;
 //     16-byte loads, each key's 256 bytes read by 16 lanes), remote keys are
@@ -23,8 +26,8 @@
 //   - V rows go through a per-wave LDS tile and come back transposed
 //     (ds_read_b64_tr_b16) as the B operand of O = P V on MFMA; the S^T
 //     accumulator layout is already P's A-operand layout.
-// The 4 waves' partial softmax statistics (row max m, row sum l, unnormalised
-// O) are merged in LDS and written to the workspace.
+// Each chunk's partial softmax statistics (row max m, row sum l, unnormalised
+// O) go to the workspace.
 // Kernel 2 (combine): per (sequence, query head) the chunk partials are
 // merged with log-sum-exp weights (Jet-Long Eq. (7)'s merge with only
 // disjoint parts) into O and the LSE.
@@ -85,22 +88,37 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   constexpr int VPL = VCHUNKS / 64;          // per lane
   constexpr int WAVES = kDThreads / 64;
   __shared__ __attribute__((aligned(16))) uint16_t vtile[WAVES][kStep * VROW];
+  __shared__ uint2 ftab[D / 2];
   __shared__ float red_m[WAVES][16], red_l[WAVES][16];
   __shared__ float red_o[WAVES][16][D + 4];
 
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // A workgroup takes one chunk of a.chunk keys for a.hpw KV heads: wave w
+  // serves head slot w % hpw and the (w / hpw)-th of the kw = 4 / hpw equal
+  // parts of the chunk. With hpw = 4 the waves read 4 heads' slices of the same
+  // rows, 4 * d * 2 contiguous bytes per row, which spreads the reads over more
+  // DRAM channels than one head's slice; each wave then owns its partial. With
+  // kw > 1 the waves of one head merge their partials in LDS.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hpw = a.hpw, kw = WAVES / a.hpw;
+  const int kvh = blockIdx.y * hpw + wave % hpw;
+  const int chunk = blockIdx.x;
+  const int b = blockIdx.z;
   const int kl = lane & 15, kg = lane >> 4;
   const int G = a.G;
+  if (MODE == kBifocal) {  // frequency table of the exact per-key phases (all waves, before any exit)
+    if (tid < D / 2) ftab[tid] = make_uint2(a.fr.lo[tid], a.fr.hi[tid]);
+    __syncthreads();
+  }
   const int L = min(max(a.kv_len[b], 0), a.Lmax);  // a length outside [0, Lmax] never reads past the cache
   const int jbeg = chunk * a.chunk;
   const size_t head_stride = size_t(a.n_chunks) * (D + 2);
   float* wsb = a.ws + (size_t(b) * a.Hq + size_t(kvh) * G) * head_stride + size_t(chunk) * (D + 2);
 
-  if (jbeg >= L) {  // chunk past this sequence's length: an empty partial
-    if (tid < G) {
-      wsb[tid * head_stride] = -INFINITY;
-      wsb[tid * head_stride + 1] = 0.f;
+  if (jbeg >= L) {  // chunk past this sequence's length: empty partials (whole workgroup)
+    if (lane < G && wave < hpw) {
+      wsb[lane * head_stride] = -INFINITY;
+      wsb[lane * head_stride + 1] = 0.f;
     }
     return;
   }
@@ -147,16 +165,14 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   // each pair's phase (2^-32 turn units) advances by a fixed increment; the
   // carries dropped from the low 32 bits cost at most 2^-32 turn per step.
   // Otherwise every phase is formed exactly from the frequency table in LDS.
-  __shared__ uint2 ftab[D / 2];
   const int sdiv = static_cast<int>(sdv.div);
   const bool affine = a.interp || (16 % sdiv) == 0;
   uint32_t ph[KSTEPS][4], inc[KSTEPS][4];
   // this wave's keys
-  const int per_wave = a.chunk / WAVES;
-  const int wbeg = jbeg + wave * per_wave;
+  const int per_wave = a.chunk / kw;
+  const int wbeg = jbeg + (wave / hpw) * per_wave;
   const int wend = min(jend, wbeg + per_wave);
   if (MODE == kBifocal) {
-    if (tid < D / 2) ftab[tid] = make_uint2(a.fr.lo[tid], a.fr.hi[tid]);
     const int dk0 = corr(wbeg + kl);
     const int d16 = a.interp ? 16 : affine ? 16 / sdiv - 16 : 0;
 #pragma unroll
@@ -167,7 +183,6 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
         ph[ks][e] = phase_top(dk0, a.fr.lo[pi], a.fr.hi[pi]);
         inc[ks][e] = phase_top(d16, a.fr.lo[pi], a.fr.hi[pi]);
       }
-    __syncthreads();
   }
 
   const uint32_t rowk_b = uint32_t(a.Hkv) * D * 2;
@@ -310,9 +325,24 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
     }
   }
 
-  // ---- merge the 4 waves' partials ------------------------------------------
-  // lane (kl, kg=0) owns head kl's m and l; O[head 4kg + i][dim 16db + kl]
+  // ---- partials: lane (kl, kg=0) holds head kl's m and l; O[head 4kg + i][dim 16db + kl]
   const float l_all = xgroup_sum(l_run);  // all lanes active for the cross-lane exchange
+  if (kw == 1) {  // the wave's partial is the chunk's
+    if (kg == 0 && kl < G) {
+      wsb[kl * head_stride] = m_run;
+      wsb[kl * head_stride + 1] = l_all;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * kg + i;
+      if (g < G) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) wsb[g * head_stride + 2 + 16 * db + kl] = oacc[db][i];
+      }
+    }
+    return;
+  }
+  // merge the kw partials of each head slot in LDS
   if (kg == 0) {
     red_m[wave][kl] = m_run;
     red_l[wave][kl] = l_all;
@@ -322,20 +352,20 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
 #pragma unroll
     for (int i = 0; i < 4; ++i) red_o[wave][4 * kg + i][16 * db + kl] = oacc[db][i];
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kDThreads) {
-    const int g = idx / D, dd = idx % D;
+  for (int idx = tid; idx < hpw * G * D; idx += kDThreads) {
+    const int hs = idx / (G * D), g = (idx / D) % G, dd = idx % D;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, red_m[w][g]);
+    for (int q = 0; q < kw; ++q) M = fmaxf(M, red_m[hs + q * hpw][g]);
     const float Mref = M == -INFINITY ? 0.f : M;
     float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
+    for (int q = 0; q < kw; ++q) {
+      const int w = hs + q * hpw;
       const float wt = __builtin_amdgcn_exp2f(red_m[w][g] - Mref);
       acc = fmaf(wt, red_o[w][g][dd], acc);
       lsum = fmaf(wt, red_l[w][g], lsum);
     }
-    float* dst = wsb + size_t(g) * head_stride;
+    float* dst = a.ws + (size_t(b) * a.Hq + size_t(blockIdx.y * hpw + hs) * G + g) * head_stride +
+                 size_t(chunk) * (D + 2);
     dst[2 + dd] = acc;
     if (dd == 0) {
       dst[0] = M;
@@ -349,8 +379,8 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
 // its own running max as it goes (the same log-sum-exp algebra as the split
 // kernel), and the CG partial merges are combined once in LDS.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a) {
-  constexpr int NT = 256;
+__global__ __launch_bounds__(1024) void decode_combine_kernel(const DecodeArgs a) {
+  constexpr int NT = 1024;
   constexpr int DV = D / 4;       // float4 columns per partial
   constexpr int CG = NT / DV;     // chunk groups
   __shared__ float sm[CG], sl[CG];
@@ -416,11 +446,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a)
 
 template <int D, int MODE>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, MODE>), dim3(a.n_chunks, a.Hkv, a.B), dim3(kDThreads), 0,
+  hipLaunchKernelGGL((decode_split_kernel<D, MODE>), dim3(a.n_chunks, a.Hkv / a.hpw, a.B), dim3(kDThreads), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.B), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

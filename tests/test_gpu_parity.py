@@ -321,6 +321,13 @@ DEC_SMALL = [
     ("multi_chunk_s3_d64", (2, 4500, 16, 4, 64), "bifocal", dict(rope_base=1e6, remap_scale=3, window_left=1000),
      [4500, 4096]),
     ("multi_chunk_nope_window", (1, 5000, 8, 8, 128), "nope", dict(window_left=2100), [5000]),
+    # Hkv % 4 == 0 and a grid of at most one workgroup per CU: each workgroup
+    # takes 4 KV heads of 1024-key chunks, one wave per head, no LDS merge
+    ("rows_layout_ragged", (3, 5000, 32, 8, 128), "bifocal", dict(rope_base=1e6, remap_scale=4, window_left=1500),
+     [5000, 1, 2049]),
+    ("rows_layout_interp_d64", (2, 3100, 16, 4, 64), "bifocal",
+     dict(rope_base=1e4, remap_scale=2, window_left=100, remote_map="interp"), [3100, 1024]),
+    ("rows_layout_rope_window", (1, 4500, 8, 4, 128), "rope", dict(rope_base=1e4, window_left=1030), [4500]),
     # interpolated remote frequencies (Jet-Long section 4.5)
     ("interp_multi_chunk", (3, 5000, 8, 2, 128), "bifocal",
      dict(rope_base=1e6, remap_scale=4, window_left=300, remote_map="interp"), [5000, 1, 4097]),
