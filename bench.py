@@ -66,26 +66,56 @@ def load_traffic(tag: str, sha: str):
     return t.get("bytes_per_launch")
 
 
+def warm_for(fn, seconds: float):
+    """Run fn back to back for about `seconds` (synchronising every 16 calls):
+    after a host-side pause (input generation) the device first runs its
+    short kernels at lower, changing clocks, which a few warm-up steps of a
+    100 us kernel do not cover."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def time_steady(fn, steps: int, warmup: int, min_seconds: float = 0.0):
+    """After ~150 ms of warm-up, time `steps` steps, or more if they would
+    take under `min_seconds` (a 100 us step is short next to the device's
+    clock changes). Returns (ms per step, steps timed)."""
+    warm_for(fn, 0.15)
+    if min_seconds > 0:
+        est, _ = time_launches(fn, 3, 0)
+        steps = max(steps, math.ceil(min_seconds * 1e3 / max(est, 1e-4)))
+    avg, _ = time_launches(fn, steps, warmup)
+    return avg, steps
+
+
 def time_launches(fn, steps: int, warmup: int):
+    """Average ms per step over `steps` steps, from one pair of events on the
+    launch stream around all of them (synchronised on both sides), and the
+    host wall time. A marker per step would put ~10 us of command-processor
+    work between consecutive kernels, which a 100 us decode step cannot hide."""
     import torch
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record()
     for i in range(steps):
-        starts[i].record()
         fn(i)
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return ms, wall
+    return start.elapsed_time(end) / steps, wall
 
 
-def bench_prefill(name, steps, warmup, unfused=False):
+def bench_prefill(name, steps, warmup, unfused=False, min_seconds=0.0):
     import torch
     import position_remapped_rope_amd as P
     import workloads as W
@@ -112,13 +142,12 @@ def bench_prefill(name, steps, warmup, unfused=False):
         def step(_):
             P.prefill(q, k, v, pos, mode=w.mode, out=o, **kw)
 
-    log(f"{name}: timing {steps} launches" + (" (unfused)" if unfused else ""))
-    ms, wall = time_launches(step, steps, warmup)
+    log(f"{name}: timing" + (" (unfused)" if unfused else ""))
+    avg, steps = time_steady(step, steps, warmup, min_seconds)
     flops = prefill_flops(w)
-    avg = sum(ms) / len(ms)
     tflops = flops / (avg * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
-    return w, inp, dict(ms=ms, avg_ms=avg, wall_s=wall, flops=flops, tflops=tflops, frac=tflops / peak)
+    return w, inp, dict(avg_ms=avg, steps_timed=steps, flops=flops, tflops=tflops, frac=tflops / peak)
 
 
 def bench_decode(name, steps, warmup):
@@ -145,11 +174,10 @@ def bench_decode(name, steps, warmup):
         kc, vc = caches[i % copies]
         P.decode(q, kc, vc, kv_len, mode="bifocal", out=o, workspace=ws, **kw)
 
-    log(f"{name}: timing {steps} launches over {copies} cache copies")
-    ms, wall = time_launches(step, steps, warmup)
-    avg = sum(ms) / len(ms)
+    log(f"{name}: timing over {copies} cache copies")
+    avg, steps = time_steady(step, steps, warmup, min_seconds=0.1)
     gbs = kv_bytes / (avg * 1e-3) / 1e9
-    return dict(ms=ms, avg_ms=avg, bytes=kv_bytes, gbs=gbs, frac=gbs / PEAK_HBM_GBS, copies=copies)
+    return dict(avg_ms=avg, bytes=kv_bytes, gbs=gbs, frac=gbs / PEAK_HBM_GBS, copies=copies, steps_timed=steps)
 
 
 def bench_copy(steps, warmup, nbytes=1 << 30):
@@ -162,8 +190,7 @@ def bench_copy(steps, warmup, nbytes=1 << 30):
     def step(_):
         torch.mul(x, 1.0, out=y)
 
-    ms, wall = time_launches(step, steps, warmup)
-    avg = sum(ms) / len(ms)
+    avg, _ = time_steady(step, steps, warmup, min_seconds=0.1)
     return dict(avg_ms=avg, read_bytes=nbytes, write_bytes=nbytes, gbs=2 * nbytes / (avg * 1e-3) / 1e9)
 
 
@@ -180,8 +207,7 @@ def bench_rope_apply(steps, warmup, S=131072, H=8, d=128):
     def step(_):
         P.rope_apply(x, pos, 1e6, out=y)
 
-    ms, _ = time_launches(step, steps, warmup)
-    avg = sum(ms) / len(ms)
+    avg, _ = time_steady(step, steps, warmup, min_seconds=0.1)
     nbytes = 2 * x.numel() * x.element_size()
     return dict(avg_ms=avg, bytes=nbytes, gbs=nbytes / (avg * 1e-3) / 1e9)
 
@@ -198,8 +224,7 @@ def bench_gemm(steps, warmup, n=8192):
     def step(_):
         torch.mm(a, b, out=c)
 
-    ms, _ = time_launches(step, steps, warmup)
-    avg = sum(ms) / len(ms)
+    avg, _ = time_steady(step, steps, warmup)
     return dict(avg_ms=avg, tflops=2.0 * n ** 3 / (avg * 1e-3) / 1e12)
 
 
@@ -254,11 +279,9 @@ def main():
         elif args.only.startswith("prefill"):
             name = "bifocal_128k" if args.only == "prefill_128k" else "bifocal_64k"
             _, _, r = bench_prefill(name, args.steps, args.warmup, unfused=args.only.endswith("unfused"))
-            r.pop("ms")
         else:
             name = "bifocal_decode_128k_b1" if args.only == "decode_b1" else "bifocal_decode_128k_b8"
             r = bench_decode(name, args.steps, args.warmup)
-            r.pop("ms")
         print(json.dumps({"only": args.only, "workload": name, **r}), flush=True)
         return
 
@@ -297,14 +320,15 @@ def main():
                                             "fused_speedup": round(unf["avg_ms"] / pre["avg_ms"], 3)}
         # the other prefill workloads: P-RoPE local + NoPE global layers at 8K, EndPrompt in fp32
         for name, st in (("prope_local_8k", 20), ("nope_global_8k", 20), ("endprompt_fp32", 50)):
-            _, _, r = bench_prefill(name, st, 3)
+            _, _, r = bench_prefill(name, st, 3, min_seconds=0.1)
             extra[name] = {"tflops": round(r["tflops"], 2), "avg_ms": round(r["avg_ms"], 4), "flop": r["flops"],
                            "frac_peak": round(r["frac"], 4),
                            "peak": "bf16 MFMA 2500" if name != "endprompt_fp32" else "fp32 vector 157.3"}
         for name, st in (("bifocal_decode_128k_b1", 50), ("bifocal_decode_128k_b8", 10)):
             d = bench_decode(name, st, 3)
             extra[name] = {"gbs": round(d["gbs"], 1), "frac_hbm_peak": round(d["frac"], 4),
-                           "avg_us": round(d["avg_ms"] * 1e3, 2), "kv_bytes": d["bytes"],
+                           "avg_us": round(d["avg_ms"] * 1e3, 2), "steps_timed": d["steps_timed"],
+                           "kv_bytes": d["bytes"],
                            "cache_copies": d["copies"]}
             torch.cuda.empty_cache()
         ra = bench_rope_apply(20, 3)

@@ -370,6 +370,75 @@ def test_decode_empty_sequences(mode, kw):
     assert float(np.max(np.abs(lse[[1, 3]] - lse_ref[[1, 3]]))) < LSE_TOL["bf16"]
 
 
+def _replay_checks(graph, out, ref, eager_fn, reps=3):
+    """Replay a captured graph several times, with eager work and synchronisation
+    between replays, and check every replay against the eager result."""
+    for r in range(reps):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), r
+        eager_fn()
+        torch.cuda.synchronize()
+
+
+def test_decode_graph_replay_matches_eager():
+    """Decode captured in a HIP graph (both layouts: 4 heads per workgroup, and
+    1 head with the LDS merge) replays to the eager result."""
+    dev = torch.device("cuda:0")
+    for B, L, Hq, Hkv, lens in ((2, 3000, 32, 8, [3000, 1700]), (2, 3000, 8, 2, [3000, 5])):
+        w = W.Workload("t", "decode", B=B, S=L, Hq=Hq, Hkv=Hkv, d=128, dtype="bf16", mode="bifocal",
+                       rope_base=1e6, seed=616)
+        inp = W.make_decode_inputs(w)
+        q, kc, vc = (inp[n].to(dev) for n in ("q", "k_cache", "v_cache"))
+        kv_len = torch.tensor(lens, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        ws = torch.empty(P.decode_workspace_size(B, L, Hq, 128), dtype=torch.uint8, device=dev)
+        kw = dict(rope_base=1e6, remap_scale=4, window_left=600)
+        run = lambda: P.decode(q, kc, vc, kv_len, mode="bifocal", out=o, workspace=ws, **kw)
+        run()
+        torch.cuda.synchronize()
+        ref = o.clone()
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            run()
+        torch.cuda.synchronize()
+        _replay_checks(g, o, ref, run)
+
+
+def test_prefill_queued_graph_replay_matches_eager():
+    """The queued prefill captured in a HIP graph: the capture stream's queue
+    buffer is left zero by every replay, so replays keep matching."""
+    dev = torch.device("cuda:0")
+    inp = _inputs(1, 3000, 8, 2, 128, "bf16", seed=617)
+    q, k, v, pos = (inp[n].to(dev) for n in ("q", "k", "v", "pos"))
+    o = torch.empty_like(q)
+    kw = dict(rope_base=1e6, remap_scale=2, window_left=500)
+    run = lambda: P.prefill(q, k, v, pos, mode="bifocal", out=o, **kw)
+    run()
+    torch.cuda.synchronize()
+    ref = o.clone()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        run()  # creates the side stream's queue buffer before capture
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        run()
+    torch.cuda.synchronize()
+    _replay_checks(g, o, ref, run)
+    assert int(P.prefill_queue(dev, side.cuda_stream).count_nonzero()) == 0
+
+
 def test_decode_workspace_reuse():
     """One workspace serves consecutive calls with other lengths: each result is
     bit-identical to a call with a fresh workspace (no state survives a call)."""
