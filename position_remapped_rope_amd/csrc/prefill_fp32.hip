@@ -16,6 +16,28 @@ namespace {
 constexpr int kBNf = 32;
 constexpr int kThreadsF = 256;
 
+// Sum over the N = 8 or 16 adjacent lanes that share a query row, with DPP
+// lane permutations inside the VALU (no LDS round trip): swap with lane ^ 1,
+// then ^ 2 (each lane now holds its quad's sum), then lane i with 7 - i of its
+// group of 8 (the two quads), then, for 16, lane i with 15 - i of its row.
+template <int N>
+__device__ __forceinline__ float row_group_sum(float x) {
+  static_assert(N == 8 || N == 16, "lanes per row");
+  auto dpp = [](float v, int ctrl) {
+    switch (ctrl) {  // the control must be a constant expression
+      case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+      case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+      case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+      default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+    }
+  };
+  x += dpp(x, 0);  // quad_perm [1,0,3,2]
+  x += dpp(x, 1);  // quad_perm [2,3,0,1]
+  x += dpp(x, 2);  // row_half_mirror
+  if (N == 16) x += dpp(x, 3);  // row_mirror
+  return x;
+}
+
 template <int MODE>
 __device__ __forceinline__ int rot_index_f(int p, int rot, const PrefillArgs& a) {
   if (rot == 2) return static_cast<int>(fastdiv(static_cast<uint32_t>(p), a.scale_div));
@@ -149,8 +171,7 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < DH; ++c) acc = fmaf(q[c], Ks[n][part * DH + c], acc);
-#pragma unroll
-        for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
+        acc = row_group_sum<TPR>(acc);
         const int dist = i - (j0 + n);
         const bool keep = dist >= dlo[p] && dist <= dhi[p];
         sc[n] = keep ? acc * sl2 : -INFINITY;
