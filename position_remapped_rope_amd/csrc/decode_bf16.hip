@@ -304,41 +304,38 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
       rs += pv[i] + pv[4 + i];
     }
     l_run = l_run * alpha + rs;
-    // P as the A operand: lane (head kl, group kg) k-slots 8kg + e are keys
+    // P^T as the B operand: lane (head kl, group kg) k-slots 8kg + e are keys
     // 4kg + e (block 0) and 16 + 4kg + e - 4 (block 1): exactly its registers
     const u32x4_t pop = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
                          pack_bf16(pv[6], pv[7])};
-    // O rows are heads 4kg + i: rescale by those heads' alpha (held by lanes kl = 4kg + i)
-    float arow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, 4 * kg + i, 16);
+    // O^T is accumulated, so a lane's O values belong to its own head kl and
+    // take its own alpha
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[db][i] *= arow[i];
-    // -- O += P V: V^T operand rows (keys) 4kg..4kg+3 and 16+4kg.., column kl of each 16-dim block
+      for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha;
+    // -- O^T += V^T P^T: V^T operand rows = dims kl of each 16-dim block, k-slots = the keys above
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       const u32x2_t va = lds_read_tr16(&vt[trow * VROW + 16 * db + tcol]);
       const u32x2_t vb = lds_read_tr16(&vt[(trow + 16) * VROW + 16 * db + tcol]);
-      oacc[db] = mfma16x16x32(pop, u32x4_t{va[0], va[1], vb[0], vb[1]}, oacc[db]);
+      oacc[db] = mfma16x16x32(u32x4_t{va[0], va[1], vb[0], vb[1]}, pop, oacc[db]);
     }
   }
 
-  // ---- partials: lane (kl, kg=0) holds head kl's m and l; O[head 4kg + i][dim 16db + kl]
+  // ---- partials: lane (kl, kg=0) holds head kl's m and l; lane (kl, kg) holds
+  // O[head kl][dims 16db + 4kg + i]
   const float l_all = xgroup_sum(l_run);  // all lanes active for the cross-lane exchange
   if (kw == 1) {  // the wave's partial is the chunk's
     if (kg == 0 && kl < G) {
       wsb[kl * head_stride] = m_run;
       wsb[kl * head_stride + 1] = l_all;
     }
+    if (kl < G) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = 4 * kg + i;
-      if (g < G) {
+      for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) wsb[g * head_stride + 2 + 16 * db + kl] = oacc[db][i];
-      }
+        for (int i = 0; i < 4; ++i) wsb[kl * head_stride + 2 + 16 * db + 4 * kg + i] = oacc[db][i];
     }
     return;
   }
@@ -350,7 +347,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red_o[wave][4 * kg + i][16 * db + kl] = oacc[db][i];
+    for (int i = 0; i < 4; ++i) red_o[wave][kl][16 * db + 4 * kg + i] = oacc[db][i];
   __syncthreads();
   for (int idx = tid; idx < hpw * G * D; idx += kDThreads) {
     const int hs = idx / (G * D), g = (idx / D) % G, dd = idx % D;
