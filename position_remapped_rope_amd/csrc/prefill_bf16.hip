@@ -15,7 +15,10 @@
 // rows: HG query heads of one KV group times BMp = 256/HG consecutive
 // positions. Each wave owns 32 rows = 32 positions of one head. All query
 // heads that read the same KV head sit in one workgroup when possible (HG = 4,
-// 2 or 1), so each K tile rotated into LDS is shared by all of them.
+// 2 or 1), so each K tile rotated into LDS is shared by all of them. Such a
+// set of rows is one work item: a launch either runs one item per workgroup,
+// or (with a work queue) a persistent workgroup per compute unit takes items
+// from per-XCD queues until they are empty.
 //
 // Bifocal merge. The workgroup walks the remote keys first (queries and keys
 // rotated at floor(p/s)), then the local window (rotated at p), carrying one
