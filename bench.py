@@ -150,11 +150,11 @@ def bench_prefill(name, steps, warmup, unfused=False, min_seconds=0.0):
     return w, inp, dict(avg_ms=avg, steps_timed=steps, flops=flops, tflops=tflops, frac=tflops / peak)
 
 
-def bench_decode(name, steps, warmup):
+def bench_decode(name, steps, warmup, S=None):
     import torch
     import position_remapped_rope_amd as P
     import workloads as W
-    w = W.get(name)
+    w = W.get(name) if S is None else W.get(name).with_(S=S)
     log(f"{name}: generating inputs")
     inp = W.make_decode_inputs(w)
     dev = torch.device("cuda:0")
@@ -331,6 +331,13 @@ def main():
                            "kv_bytes": d["bytes"],
                            "cache_copies": d["copies"]}
             torch.cuda.empty_cache()
+        # not a benchmark configuration: the same decode on a 16K cache, where the
+        # launch shrinks its chunks to keep the chip busy (latency-bound, for scale)
+        d = bench_decode("bifocal_decode_128k_b1", 50, 3, S=16384)
+        extra["bifocal_decode_16k_b1"] = {"gbs": round(d["gbs"], 1), "frac_hbm_peak": round(d["frac"], 4),
+                                          "avg_us": round(d["avg_ms"] * 1e3, 2), "kv_bytes": d["bytes"],
+                                          "note": "16K cache, not a benchmark configuration"}
+        torch.cuda.empty_cache()
         ra = bench_rope_apply(20, 3)
         extra["rope_apply_128k_k"] = {"gbs": round(ra["gbs"], 1), "frac_hbm_peak": round(ra["gbs"] / PEAK_HBM_GBS, 4),
                                       "avg_us": round(ra["avg_ms"] * 1e3, 2), "bytes": ra["bytes"]}

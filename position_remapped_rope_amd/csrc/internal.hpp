@@ -66,17 +66,6 @@ struct DecodeArgs {
                       // theta_i / s - theta_i (interpolation, index p)
 };
 
-// Decode split: a workgroup takes a chunk of keys for hpw KV heads.
-//  - 4 heads x 1024 keys (one wave per head) when Hkv % 4 == 0 and that grid
-//    has at most one workgroup per compute unit (batch 1 at 128K): the 4 heads'
-//    slices of a row are contiguous, which measured 5% faster than one head
-//    per workgroup, the combine aside;
-//  - else 1 head x 4096 keys when that grid fits in one round, else 2048.
-// The workspace is sized for the smallest chunk.
-constexpr int kDecodeChunkRows = 1024;
-constexpr int kDecodeChunk = 2048;
-constexpr int kDecodeChunkLarge = 4096;
-
 // Fill F_i = round(theta_i / (2 pi s) * 2^64), theta_i = base^(-2i/d), in long double.
 void fill_rope_freq(RopeFreq& f, int d, double base, int s = 1);
 

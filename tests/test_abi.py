@@ -168,9 +168,10 @@ def test_prefill_queued_rejects(kw):
 
 def test_workspace_size_formula():
     L = P.lib()
-    # [B][Hq][ceil(Lmax / 1024)][d + 2] float32 partials
-    assert L.prope_decode_workspace_size(1, 131072, 32, 128) == 1 * 32 * 128 * 130 * 4
-    assert L.prope_decode_workspace_size(8, 3000, 4, 64) == 8 * 4 * 3 * 66 * 4
+    # [B][Hq][chunks][d + 2] float32 partials, chunks = max(ceil(Lmax / 1024), min(512, ceil(Lmax / 128)))
+    assert L.prope_decode_workspace_size(1, 131072, 32, 128) == 1 * 32 * 512 * 130 * 4
+    assert L.prope_decode_workspace_size(8, 3000, 4, 64) == 8 * 4 * 24 * 66 * 4
+    assert L.prope_decode_workspace_size(1, 1 << 20, 8, 128) == 1 * 8 * 1024 * 130 * 4
     assert L.prope_decode_workspace_size(0, 10, 4, 64) == 0
 
 
