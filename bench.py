@@ -7,8 +7,10 @@ bifocal merge). The same JSON line also carries the 128K bifocal prefill and
 the 128K-cache bifocal decode (batch 1 and 8), each timed the same way.
 
 Prints ONE JSON line. Inputs are seeded synthetic N(0,1) tensors (workloads/),
-resident in HBM before timing starts. Kernel time comes from HIP events on the
-stream the kernels run on.
+resident in HBM before timing starts. Each leg runs ~150 ms of warm-up steps;
+its time per step is one pair of HIP events on the stream the kernels run on,
+around all timed steps (exactly --steps for the headline leg, at least 100 ms
+of work for the short legs).
 """
 from __future__ import annotations
 
