@@ -1,11 +1,16 @@
 // float32 prefill: same scores, masks and bifocal routing as the bf16 kernel,
-// computed with fp32 vector ALU (no operand rounding). D / 8 adjacent lanes
-// share one query row of one head, 8 dims each, and reduce each score with
-// lane shuffles; K (rotated in fp32) and V tiles of 32 keys are staged in LDS,
-// the next tile's loads in flight while the current one is processed.
-// Meant for small fp32 problems such as the EndPrompt two-segment check: the
-// narrow row split gives a 256-token problem enough workgroups to spread over
-// the chip. The bf16 MFMA kernel is the throughput path.
+// computed with fp32 vector ALU (no operand rounding). Meant for small fp32
+// problems such as the EndPrompt two-segment check; the bf16 MFMA kernel is
+// the throughput path.
+//
+// A workgroup of 8 waves owns a few query rows (64 / (D/8) of them: D/8
+// adjacent lanes share a row, 8 dims each) and splits their keys: wave w takes
+// every 8th 16-key tile of each pass, stages it (K rotated in fp32) in its own
+// LDS slot, and keeps its own softmax statistics (m, l, O) for the rows. The
+// 8 partial states are merged once at the end (the log-sum-exp algebra of
+// Jet-Long Eq. (7) with disjoint parts). With the keys split this way a
+// row's tiles run 8 at a time instead of one after another: a short problem
+// is bound by the latency of its longest rows' tile loop, at one wave per SIMD.
 #include <limits.h>
 
 #include "internal.hpp"
@@ -13,8 +18,9 @@
 namespace prope {
 namespace {
 
-constexpr int kBNf = 32;
-constexpr int kThreadsF = 256;
+constexpr int kBNf = 16;         // keys per tile
+constexpr int kWavesF = 8;       // key groups per workgroup
+constexpr int kThreadsF = 64 * kWavesF;
 
 // Sum over the N = 8 or 16 adjacent lanes that share a query row, with DPP
 // lane permutations inside the VALU (no LDS round trip): swap with lane ^ 1,
@@ -45,20 +51,24 @@ __device__ __forceinline__ int rot_index_f(int p, int rot, const PrefillArgs& a)
   return p;
 }
 
-// TPR = D / 8 lanes share one query row, each owning 8 of its dims; a
-// workgroup covers 256 / TPR rows (HG heads x BMp positions, set by the launcher).
+// A workgroup covers RPW = 64 / TPR rows (HG heads x BMp = RPW / HG positions,
+// set by the launcher); each of its 8 waves holds all of them.
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillArgs a) {
-  constexpr int DH = 8;                            // dims per lane
-  constexpr int TPR = D / DH;                      // lanes per query row
-  constexpr int NPR = D / 2;                       // pairs per row
-  constexpr int PAIRS = kBNf * NPR / kThreadsF;    // pairs staged per thread
-  constexpr int RPS = kThreadsF / NPR;             // rows per staging sweep
-  __shared__ __attribute__((aligned(16))) float Ks[kBNf][D];
-  __shared__ __attribute__((aligned(16))) float Vs[kBNf][D];
+  constexpr int DH = 8;                  // dims per lane
+  constexpr int TPR = D / DH;            // lanes per query row
+  constexpr int RPW = 64 / TPR;          // rows per workgroup (every wave holds them all)
+  constexpr int NPR = D / 2;             // pairs per key row
+  constexpr int PAIRS = kBNf * NPR / 64; // pairs a lane stages per tile
+  constexpr int KPS = 64 / NPR;          // keys one staging sweep of the wave covers
+  __shared__ __attribute__((aligned(16))) float Ks[kWavesF][kBNf][D];
+  __shared__ __attribute__((aligned(16))) float Vs[kWavesF][kBNf][D];
+  __shared__ float red_m[kWavesF][RPW], red_l[kWavesF][RPW];
+  __shared__ __attribute__((aligned(16))) float red_o[kWavesF][RPW][D];
 
-  const int tid = threadIdx.x;
-  const int row = tid / TPR, part = tid % TPR;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane / TPR, part = lane % TPR;
   int item = xcd_remap(blockIdx.x, gridDim.x);
   const int pb = a.n_pblocks - 1 - (item % a.n_pblocks);
   item /= a.n_pblocks;
@@ -91,7 +101,9 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
     npass = 1;
   }
 
-  const int spair = tid % NPR;  // pair this thread stages (same for every row it stages)
+  const int spair = lane % NPR;  // pair this lane stages (the same in every key it stages)
+  float (*ks)[D] = Ks[wave];
+  float (*vs)[D] = Vs[wave];
 
   float o[DH], q[DH];
 #pragma unroll
@@ -125,13 +137,15 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
     const int64_t jlo = max<int64_t>(0, int64_t(P0) - dhi[p]);
     const int64_t jhi = min<int64_t>(S - 1, int64_t(P1) - dlo[p]);
     if (jhi < jlo) continue;
-    // this thread's K/V pairs and ids of one tile, loaded a tile ahead
+    // this wave's tiles of the pass: every kWavesF-th, starting at tile `wave`
+    const int t_first = static_cast<int>(jlo / kBNf), t_last = static_cast<int>(jhi / kBNf);
+    // this lane's K/V pairs and ids of one tile, loaded a tile ahead
     float2 kr[PAIRS], vr[PAIRS];
     int jid[PAIRS];
     auto load_tile = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) {
-        const int j = j0 + tid / NPR + RPS * u;
+        const int j = j0 + u * KPS + lane / NPR;
         kr[u] = vr[u] = make_float2(0.f, 0.f);
         jid[u] = 0;
         if (j < S) {
@@ -141,13 +155,15 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
         }
       }
     };
-    const int jfirst = static_cast<int>(jlo / kBNf) * kBNf;
-    load_tile(jfirst);
-    for (int j0 = jfirst; j0 <= jhi; j0 += kBNf) {
-      __syncthreads();
+    int t = t_first + wave;
+    if (t <= t_last) load_tile(t * kBNf);
+    for (; t <= t_last; t += kWavesF) {
+      const int j0 = t * kBNf;
+      // stage this tile in the wave's own LDS slot (the wave alone reads it,
+      // and its LDS operations complete in order: no workgroup barrier)
 #pragma unroll
       for (int u = 0; u < PAIRS; ++u) {
-        const int n = tid / NPR + RPS * u;
+        const int n = u * KPS + lane / NPR;
         float x0 = kr[u].x, x1 = kr[u].y;
         if (MODE != kNope && rot[p] && j0 + n < S) {
           float s, c;
@@ -157,23 +173,22 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
           x0 = y0;
           x1 = y1;
         }
-        Ks[n][2 * spair] = x0;
-        Ks[n][2 * spair + 1] = x1;
-        Vs[n][2 * spair] = vr[u].x;
-        Vs[n][2 * spair + 1] = vr[u].y;
+        ks[n][2 * spair] = x0;
+        ks[n][2 * spair + 1] = x1;
+        vs[n][2 * spair] = vr[u].x;
+        vs[n][2 * spair + 1] = vr[u].y;
       }
-      __syncthreads();
-      if (j0 + kBNf <= jhi) load_tile(j0 + kBNf);  // in flight during this tile's math
+      if (t + kWavesF <= t_last) load_tile((t + kWavesF) * kBNf);  // in flight during this tile's math
       float sc[kBNf];
       float mx = -INFINITY;
 #pragma unroll
       for (int n = 0; n < kBNf; ++n) {
         float acc = 0.f;
 #pragma unroll
-        for (int c = 0; c < DH; ++c) acc = fmaf(q[c], Ks[n][part * DH + c], acc);
+        for (int c = 0; c < DH; ++c) acc = fmaf(q[c], ks[n][part * DH + c], acc);
         acc = row_group_sum<TPR>(acc);
         const int dist = i - (j0 + n);
-        const bool keep = dist >= dlo[p] && dist <= dhi[p];
+        const bool keep = dist >= dlo[p] && dist <= dhi[p] && j0 + n < S;
         sc[n] = keep ? acc * sl2 : -INFINITY;
         mx = fmaxf(mx, sc[n]);
       }
@@ -189,25 +204,48 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
         const float pv = __builtin_amdgcn_exp2f(sc[n] - mref);
         l_run += pv;
 #pragma unroll
-        for (int c = 0; c < DH; ++c) o[c] = fmaf(pv, Vs[n][part * DH + c], o[c]);
+        for (int c = 0; c < DH; ++c) o[c] = fmaf(pv, vs[n][part * DH + c], o[c]);
       }
     }
   }
-  if (!valid) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  float* og = static_cast<float*>(a.o) + size_t(b) * S * rowq + size_t(h) * D + size_t(i) * rowq + part * DH;
+
+  // merge the 8 waves' statistics of each row
+  if (part == 0) {
+    red_m[wave][row] = m_run;
+    red_l[wave][row] = l_run;
+  }
 #pragma unroll
-  for (int c = 0; c < DH; c += 4)
-    *reinterpret_cast<float4*>(og + c) = make_float4(o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv);
-  if (a.lse && part == 0)
-    a.lse[(size_t(b) * a.Hq + h) * S + i] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+  for (int c = 0; c < DH; ++c) red_o[wave][row][part * DH + c] = o[c];
+  __syncthreads();
+  for (int idx = tid; idx < RPW * D; idx += kThreadsF) {
+    const int r = idx / D, dd = idx % D;
+    const int hr = r / a.BMp;
+    const int ir = P0 + r - hr * a.BMp;
+    if (ir >= S) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWavesF; ++w) M = fmaxf(M, red_m[w][r]);
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWavesF; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(red_m[w][r] - Mref);
+      acc = fmaf(wt, red_o[w][r][dd], acc);
+      lsum = fmaf(wt, red_l[w][r], lsum);
+    }
+    const int hr_head = kvh * a.G + hsub * a.HG + hr;
+    float* og = static_cast<float*>(a.o) + size_t(b) * S * rowq + size_t(hr_head) * D + size_t(ir) * rowq;
+    og[dd] = lsum > 0.f ? acc / lsum : 0.f;
+    if (a.lse && dd == 0)
+      a.lse[(size_t(b) * a.Hq + hr_head) * S + ir] = lsum > 0.f ? (M + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
+  }
 }
 
 template <int D, int MODE>
 hipError_t launch_f(const PrefillArgs& a0, hipStream_t stream) {
-  // rows per workgroup = 256 / (D / 8)
+  // rows per workgroup = 64 / (D / 8), split over HG heads
   PrefillArgs a = a0;
-  a.BMp = (kThreadsF / (D / 8)) / a.HG;
+  a.BMp = (64 / (D / 8)) / a.HG;
   a.n_pblocks = (a.S + a.BMp - 1) / a.BMp;
   const int64_t n = int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks;
   hipLaunchKernelGGL((prefill_fp32_kernel<D, MODE>), dim3(static_cast<unsigned>(n)), dim3(kThreadsF), 0,
