@@ -371,10 +371,11 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   }
 }
 
-// One workgroup per (query head, sequence), one round of loads: thread
-// (cg, dv) takes chunks cg, cg + CG, ... and 4 dims of O, merges them against
-// its own running max as it goes (the same log-sum-exp algebra as the split
-// kernel), and the CG partial merges are combined once in LDS.
+// One workgroup per (query head, sequence): thread (cg, dv) takes chunks cg,
+// cg + CG, ... (one round of loads for up to 4 * CG chunks, as at 128K; short
+// caches split into more chunks take a few rounds) and 4 dims of O, merges
+// them against its own running max as it goes (the same log-sum-exp algebra as
+// the split kernel), and the CG partial merges are combined once in LDS.
 template <int D>
 __global__ __launch_bounds__(1024) void decode_combine_kernel(const DecodeArgs a) {
   constexpr int NT = 1024;
