@@ -101,7 +101,10 @@ typedef struct {
  *   Query head h reads KV head h / (Hq / Hkv); Hq % Hkv must be 0.
  *   d in {64, 128}; 1 <= S; 1 <= B; bf16 or fp32. One sequence's q slice
  *   (S * Hq * d elements) must stay under 2^30 elements (32-bit byte offsets),
- *   else PROPE_ERR_UNSUPPORTED.
+ *   else PROPE_ERR_UNSUPPORTED. So must the launch grid, at most 2^32 - 1
+ *   work-items: bf16 takes 512 threads per 256 (row, head) pairs, so it fits
+ *   any problem that fits in memory; fp32 takes 512 threads per 8 pairs at
+ *   d = 64 and per 4 at d = 128, so B * Hq * S is limited to about 2^25.
  *   Rows with no kept key (impossible: the key j = i is always kept) would
  *   get O = 0 and lse = -inf.
  */
@@ -150,6 +153,9 @@ int prope_attn_prefill_queued(const void* q, const void* k, const void* v, void*
  *     as in prope_attn_prefill_queued); too small -> PROPE_ERR_WORKSPACE. Its
  *     contents need no initialisation and are scratch after the call.
  *   Enqueues six kernels on `stream` (five for fp32, which has no queue).
+ *   Beyond prope_attn_prefill's limits, the merge takes one thread per 8
+ *   output elements: B * S * Hq * d / 8 over 2^32 - 1 -> PROPE_ERR_UNSUPPORTED.
+ *   Every check is made before the first kernel is enqueued.
  */
 size_t prope_bifocal_unfused_workspace_size(int B, int S, int Hq, int d, int dt);
 int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -175,9 +181,9 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
  *     keys beyond window_left masked. `period` must be 0.
  *   workspace: caller-owned device buffer of at least
  *     prope_decode_workspace_size(B, Lmax, Hq, d) bytes (split-K partials);
- *     too small -> PROPE_ERR_WORKSPACE. bf16 only; Hq / Hkv <= 16 and one
- *     sequence's cache slice (Lmax * Hkv * d * 2 bytes) under 4 GiB, else
- *     PROPE_ERR_UNSUPPORTED.
+ *     too small -> PROPE_ERR_WORKSPACE. bf16 only; Hq / Hkv <= 16, B and
+ *     Hkv <= 65535 (launch grid limits) and one sequence's cache slice
+ *     (Lmax * Hkv * d * 2 bytes) under 4 GiB, else PROPE_ERR_UNSUPPORTED.
  */
 size_t prope_decode_workspace_size(int B, int Lmax, int Hq, int d);
 int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

@@ -153,6 +153,11 @@ PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, f
   return a;
 }
 
+// Whether the launch grid of a prefill call fits the device's launch limits.
+bool prefill_fits(const PrefillArgs& a, int dt) {
+  return dt == PROPE_BF16 ? prefill_bf16_fits(a) : prefill_fp32_fits(a);
+}
+
 int run_prefill(const PrefillArgs& a, int dt, void* stream) {
   const hipError_t e = dt == PROPE_BF16 ? launch_prefill_bf16(a, static_cast<hipStream_t>(stream))
                                         : launch_prefill_fp32(a, static_cast<hipStream_t>(stream));
@@ -231,6 +236,7 @@ int prope_attn_prefill(const void* q, const void* k, const void* v, void* o, flo
   const int pc = check_prefill(q, k, v, o, pos, B, S, Hq, Hkv, d, dt, params);
   if (pc != PROPE_OK) return pc;
   const PrefillArgs a = prefill_args(q, k, v, o, lse, pos, B, S, Hq, Hkv, d, *params);
+  if (!prefill_fits(a, dt)) return PROPE_ERR_UNSUPPORTED;
   return run_prefill(a, dt, stream);
 }
 
@@ -245,6 +251,7 @@ int prope_attn_prefill_queued(const void* q, const void* k, const void* v, void*
   // the fp32 kernel has no queue: it runs its static schedule and leaves the buffer as it is
   uint32_t* wq = dt == PROPE_BF16 ? static_cast<uint32_t*>(queue) : nullptr;
   const PrefillArgs a = prefill_args(q, k, v, o, lse, pos, B, S, Hq, Hkv, d, *params, wq);
+  if (!prefill_fits(a, dt)) return PROPE_ERR_UNSUPPORTED;
   return run_prefill(a, dt, stream);
 }
 
@@ -264,6 +271,11 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return PROPE_ERR_INVALID_ARG;
   const UnfusedLayout ly = unfused_layout(B, S, Hq, d, dt);
   if (workspace_bytes < ly.total) return PROPE_ERR_WORKSPACE;
+  // every launch is checked against the grid limits before the first is enqueued
+  // (the three calls share one grid; the merge takes a thread per 8 elements)
+  if (!prefill_fits(prefill_args(q, k, v, o, lse, pos, B, S, Hq, Hkv, d, *params), dt) ||
+      int64_t(B) * S * Hq * (d / 8) > kMaxWorkItems)
+    return PROPE_ERR_UNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
   void* oa = ws + ly.oa;
   void* oc = ws + ly.oc;
@@ -320,6 +332,7 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
   if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
   if (dt != PROPE_BF16) return PROPE_ERR_UNSUPPORTED;
   if (Hq / Hkv > 16) return PROPE_ERR_UNSUPPORTED;  // query heads of a group fill one 16-wide MFMA tile
+  if (B > 65535 || Hkv > 65535) return PROPE_ERR_UNSUPPORTED;  // grid y and z limits
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(o) |
        reinterpret_cast<uintptr_t>(workspace)) % 16)

@@ -73,6 +73,13 @@ hipError_t launch_rope_apply(const void* x, void* y, const int32_t* pos, int B, 
                              int d, int dt, const RopeFreq& f, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_fp32(const PrefillArgs& a, hipStream_t stream);
+
+// A 1-D launch covers at most 2^32 - 1 work-items (the dispatch packet holds the
+// grid size in work-items in 32 bits). The prefill launchers' grids, as host-side
+// checks made before anything is enqueued:
+constexpr int64_t kMaxWorkItems = 0xffffffffLL;
+bool prefill_bf16_fits(const PrefillArgs& a);
+bool prefill_fp32_fits(const PrefillArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_remap_ids(const int32_t* pos, int32_t* out, int64_t n, const FastDiv& s, hipStream_t stream);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream);

@@ -818,11 +818,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   }
 }
 
+int64_t n_items(const PrefillArgs& a) { return int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks; }
+
 template <int D, int MODE>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   // one workgroup per item, or with a queue one per compute unit (a workgroup
   // fills a CU: 8 waves at 2 per SIMD)
-  const int64_t n = int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks;
+  const int64_t n = n_items(a);
   const int64_t grid = a.queue ? (n < a.n_cu ? n : a.n_cu) : n;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
                      stream, a);
@@ -830,6 +832,10 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Bounded by the static schedule's grid, one workgroup per item; the queued
+// schedule launches fewer but numbers the same items.
+bool prefill_bf16_fits(const PrefillArgs& a) { return n_items(a) * kThreads <= kMaxWorkItems; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   if (a.D == 128) {

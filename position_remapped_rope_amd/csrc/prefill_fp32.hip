@@ -241,19 +241,28 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
   }
 }
 
+// rows per workgroup = 64 / (D / 8), split over HG heads
+PrefillArgs fp32_args(const PrefillArgs& a0) {
+  PrefillArgs a = a0;
+  a.BMp = (64 / (a.D / 8)) / a.HG;
+  a.n_pblocks = (a.S + a.BMp - 1) / a.BMp;
+  return a;
+}
+
+int64_t n_blocks(const PrefillArgs& a) { return int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks; }
+
 template <int D, int MODE>
 hipError_t launch_f(const PrefillArgs& a0, hipStream_t stream) {
-  // rows per workgroup = 64 / (D / 8), split over HG heads
-  PrefillArgs a = a0;
-  a.BMp = (64 / (D / 8)) / a.HG;
-  a.n_pblocks = (a.S + a.BMp - 1) / a.BMp;
-  const int64_t n = int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks;
+  const PrefillArgs a = fp32_args(a0);
+  const int64_t n = n_blocks(a);
   hipLaunchKernelGGL((prefill_fp32_kernel<D, MODE>), dim3(static_cast<unsigned>(n)), dim3(kThreadsF), 0,
                      stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool prefill_fp32_fits(const PrefillArgs& a) { return n_blocks(fp32_args(a)) * kThreadsF <= kMaxWorkItems; }
 
 hipError_t launch_prefill_fp32(const PrefillArgs& a, hipStream_t stream) {
   if (a.D == 128) {

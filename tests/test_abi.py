@@ -88,6 +88,19 @@ def test_prefill_rejects(kw):
     assert _prefill(**kw) == INVALID
 
 
+def test_prefill_rejects_grids_beyond_the_launch_limit():
+    # a 1-D launch holds at most 2^32 - 1 work-items; the checks return before any HIP call
+    rope = _params(mode=P.ROPE, remap_scale=1)
+    # fp32 at d = 128: 4 (row, head) pairs per 512-thread workgroup, so 2^25 pairs need 2^32 threads
+    assert _prefill(B=64, S=16384, Hq=32, Hkv=32, d=128, dt=1, params=rope) == UNSUPPORTED
+    assert _prefill_queued(B=64, S=16384, Hq=32, Hkv=32, d=128, dt=1) == UNSUPPORTED
+    # bf16: 256 pairs per workgroup, 2^31 pairs (256 GiB of q at d = 64)
+    assert _prefill(B=256, S=1 << 17, Hq=64, Hkv=64, d=64, dt=0, params=rope) == UNSUPPORTED
+    # the unfused merge takes a thread per 8 outputs: 2^28 rows at d = 128, while its calls fit
+    assert _unfused(B=64, S=1 << 16, Hq=64, Hkv=64, d=128, dt=0) == UNSUPPORTED
+    assert _unfused(B=64, S=16384, Hq=32, Hkv=32, d=128, dt=1) == UNSUPPORTED
+
+
 def test_prefill_nope_allows_null_pos_but_rope_does_not():
     assert _prefill(pos=None, params=_params(mode=P.ROPE, remap_scale=1)) == INVALID
 
@@ -108,6 +121,7 @@ def _decode(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, kv_len=FAKE, B=1, Lmax=4096, Hq=32
     (dict(params=_params(mode=P.ROPE, remap_scale=1, period=16)), INVALID),
     (dict(dt=1), UNSUPPORTED), (dict(Hq=64, Hkv=2), UNSUPPORTED),
     (dict(Lmax=1 << 21, Hkv=8, Hq=32), UNSUPPORTED),
+    (dict(B=65536, Lmax=1024), UNSUPPORTED), (dict(Hq=65536, Hkv=65536, Lmax=16, d=64), UNSUPPORTED),
     (dict(ws_bytes=100), WORKSPACE),
     (dict(params=_params(remap_scale=1, w_pretrained=4096, remote_map=1)), UNSUPPORTED),
 ])
