@@ -266,7 +266,7 @@ def main():
                     help="time one leg only and print its figures (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on a single GPU (no multi-GPU path); --gpus must be 1"}))
         sys.exit(2)
 
     import torch
