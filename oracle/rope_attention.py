@@ -20,6 +20,9 @@ Sources (page titles; sections and equations named where each step is used):
 * EndPrompt (abstract): a two-segment sequence whose second segment carries
   ids near the target length; attention over it is ordinary causal RoPE
   attention on those ids.
+* "Periodic RoPE for Infinite Context LLMs", section 1: the earlier layer
+  design of sliding-window attention with ALiBi, its linear distance penalty
+  clamped to the window, with a manually set slope.
 
 Readings taken where the pages leave a step open:
 
@@ -31,7 +34,13 @@ Readings taken where the pages leave a step open:
   key); position ids drive the rotation only.
 * ``window_left`` is the largest kept distance i - j. For the P-RoPE window of
   W keys it is W - 1; for Jet-Long it is w0 (local iff i - j <= w0).
-* ``remap_scale`` is the integer group size G of Jet-Long Eq. (2)-(3).
+* ``remap_scale`` is the integer group size G of Jet-Long Eq. (2)-(3) for the
+  aliasing map. For the interpolation map it may be any real s >= 1; the
+  continuous dynamic factor of Jet-Long section 3.1 is s = max(1, L / w_pre)
+  (``continuous_scale``).
+* ALiBi (``alibi_slopes``, one slope m_h per query head, nope/rope modes): the
+  scaled score of a kept key gets - m_h * (i - j) added; keys beyond the window
+  are masked, so the penalty only acts on distances 0 .. window_left.
 * ``operand_round``: the rotated query and key that enter the score product are
   rounded once to the given type ("bf16" or "fp32"), the rest stays float64.
   This models a model that stores RoPE'd vectors in its own dtype (the Jet-Long
@@ -94,6 +103,12 @@ def group_size(L: int, w_pretrained: int) -> int:
     return max(1, -(-int(L) // int(w_pretrained)))
 
 
+def continuous_scale(L: int, w_pretrained: int) -> float:
+    """s = max(1, L / w_pretrained), the continuous-style dynamic factor (Jet-Long
+    page, section 3.1, stated beside Eq. (2) for frequency-rescaling methods)."""
+    return max(1.0, float(L) / float(w_pretrained))
+
+
 def remote_index(p, G: int):
     """f(x) = floor(x / G) (Jet-Long page, section 3.1, Eq. (3))."""
     return np.floor_divide(np.asarray(p, dtype=np.int64), int(G))
@@ -106,7 +121,7 @@ def remote_position(p, G: int, remote_map: str = "alias"):
     "interp": p / G unfloored, i.e. every frequency theta_i divided by G at the
     original positions: the frequency-interpolation mapping the same page
     compares against aliasing in section 4.5 (Table 6), taken in its plainest
-    (uniform, linear) form.
+    (uniform, linear) form. G may be any real number >= 1 here.
     """
     if remote_map == "alias":
         return remote_index(p, G)
@@ -170,20 +185,25 @@ def _softmax_rows(scores: np.ndarray, keep: np.ndarray, vals: np.ndarray):
     return o, lse
 
 
-def _check_mode(mode, period, remap_scale, window_left, remote_map="alias"):
+def _check_mode(mode, period, remap_scale, window_left, remote_map="alias", alibi_slopes=None):
     if mode not in MODES:
         raise ValueError(f"mode must be one of {MODES}")
     if period < 0 or remap_scale < 1 or window_left < -1:
         raise ValueError("bad period / remap_scale / window_left")
     if remote_map not in ("alias", "interp") or (remote_map == "interp" and mode != "bifocal"):
         raise ValueError("bad remote_map")
+    if remote_map == "alias" and int(remap_scale) != remap_scale:
+        raise ValueError("the aliasing map takes an integer group size")
+    if alibi_slopes is not None and mode == "bifocal":
+        raise ValueError("ALiBi biases apply to the nope/rope modes")
 
 
 def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0,
                 remap_scale: int = 1, window_left: int = -1,
                 softmax_scale: Optional[float] = None, operand_round: Optional[str] = None,
                 rows: Optional[np.ndarray] = None, max_block_elems: int = 1 << 24,
-                remote_map: str = "alias") -> Tuple[np.ndarray, np.ndarray]:
+                remote_map: str = "alias",
+                alibi_slopes: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Causal attention with RoPE under remapped ids, computed directly.
 
     q [B,S,Hq,d], k/v [B,S,Hkv,d] (unrotated), pos int [B,S]. The KV head of
@@ -199,9 +219,12 @@ def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0
                                                          (Jet-Long page, Eq. (1), (3)),
                             or f(x) = x / s with remote_map="interp" (section 4.5)
     then scaled by softmax_scale (default 1/sqrt(d)). In nope/rope modes a
-    window_left >= 0 also drops keys with i - j > window_left.
+    window_left >= 0 also drops keys with i - j > window_left, and
+    ``alibi_slopes`` (length Hq) adds - m_h * (i - j) to the scaled score of
+    each kept key: the sliding-window ALiBi layer of the P-RoPE page, section 1,
+    whose penalty the window clamps to distances 0 .. window_left.
     """
-    _check_mode(mode, period, remap_scale, window_left, remote_map)
+    _check_mode(mode, period, remap_scale, window_left, remote_map, alibi_slopes)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -212,6 +235,7 @@ def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0
         raise ValueError("Hq must be a multiple of Hkv")
     grp = Hq // Hkv
     scale = (1.0 / math.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float64).reshape(Hq)
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     R = rows.shape[0]
     o_out = np.zeros((B, R, Hq, d))
@@ -251,7 +275,10 @@ def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0
                 if mode == "bifocal":
                     sc_remote = qr[sel, h, :] @ kr[:jmax, g, :].T
                     sc = np.where(dist <= window_left, sc, sc_remote)
-                o, lse = _softmax_rows(sc * scale, keep, v[b, :jmax, g, :])
+                logits = sc * scale
+                if slopes is not None:
+                    logits = logits - slopes[h] * dist
+                o, lse = _softmax_rows(logits, keep, v[b, :jmax, g, :])
                 o_out[b, sel, h, :] = o
                 lse_out[b, h, sel] = lse
     return o_out, lse_out
@@ -260,7 +287,8 @@ def prefill_ref(q, k, v, pos, mode: str, rope_base: float = 1e4, period: int = 0
 def decode_ref(q, k_cache, v_cache, kv_len, mode: str = "bifocal", rope_base: float = 1e6,
                remap_scale: int = 1, window_left: int = -1,
                softmax_scale: Optional[float] = None, operand_round: Optional[str] = None,
-               remote_map: str = "alias") -> Tuple[np.ndarray, np.ndarray]:
+               remote_map: str = "alias",
+               alibi_slopes: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """One decode step against a cache of base-rotated keys.
 
     q [B,Hq,d] is the query already rotated at its own position p_q = kv_len-1;
@@ -274,9 +302,11 @@ def decode_ref(q, k_cache, v_cache, kv_len, mode: str = "bifocal", rope_base: fl
     dk_j = j/s - j.
     nope/rope: the cache and q already carry whatever rotation the layer uses,
     so scores are q . k_j, with keys p_q - j > window_left dropped if
-    window_left >= 0.
+    window_left >= 0 and, with ``alibi_slopes``, - m_h * (p_q - j) added to
+    each scaled score (as in prefill_ref).
+    A real remap_scale s with remote_map="interp" gives dq = p_q/s - p_q.
     """
-    _check_mode(mode, 0, remap_scale, window_left, remote_map)
+    _check_mode(mode, 0, remap_scale, window_left, remote_map, alibi_slopes)
     q = np.asarray(q, dtype=np.float64)
     kc = np.asarray(k_cache, dtype=np.float64)
     vc = np.asarray(v_cache, dtype=np.float64)
@@ -285,6 +315,7 @@ def decode_ref(q, k_cache, v_cache, kv_len, mode: str = "bifocal", rope_base: fl
     Hkv = kc.shape[2]
     grp = Hq // Hkv
     scale = (1.0 / math.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float64).reshape(Hq)
     o_out = np.zeros((B, Hq, d))
     lse_out = np.full((B, Hq), -np.inf)
     for b in range(B):
@@ -305,7 +336,10 @@ def decode_ref(q, k_cache, v_cache, kv_len, mode: str = "bifocal", rope_base: fl
             sc = kc[b, :L, g, :] @ q[b, h]
             if mode == "bifocal":
                 sc = np.where(dist <= window_left, sc, k_rem[:, g, :] @ q_rem[h])
-            o, lse = _softmax_rows((sc * scale)[None, :], keep[None, :], vc[b, :L, g, :])
+            logits = sc * scale
+            if slopes is not None:
+                logits = logits - slopes[h] * dist
+            o, lse = _softmax_rows(logits[None, :], keep[None, :], vc[b, :L, g, :])
             o_out[b, h] = o[0]
             lse_out[b, h] = lse[0]
     return o_out, lse_out
@@ -329,13 +363,14 @@ def _window_call(qrot, krot, v, lo_dist, hi_dist, scale):
 
 
 def bifocal_eq7_ref(q, k, v, pos, rope_base: float, remap_scale: int, window_left: int,
-                    softmax_scale: Optional[float] = None):
+                    softmax_scale: Optional[float] = None, remote_map: str = "alias"):
     """Bifocal attention by the three-call inclusion-exclusion merge.
 
     (A) window w0 with base q/k, (B) full causal with remote q/k, (C) window w0
     with remote q/k; M = max(lse_A, lse_B, lse_C), W_X = exp(lse_X - M),
     O = (W_A O_A + W_B O_B - W_C O_C) / (W_A + W_B - W_C)
-    (Jet-Long page, section 3.3, Eq. (7)). Float64, no operand rounding.
+    (Jet-Long page, section 3.3, Eq. (7)). Float64, no operand rounding. The
+    remote q/k are rotated at remote_position(p, s, remote_map).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -348,7 +383,7 @@ def bifocal_eq7_ref(q, k, v, pos, rope_base: float, remap_scale: int, window_lef
     out = np.zeros_like(q)
     for b in range(B):
         p = pos[b]
-        rr = remote_index(p, remap_scale)
+        rr = remote_position(p, remap_scale, remote_map)
         for h in range(Hq):
             g = h // grp
             qb = rotate(q[b, :, h], p, rope_base)
@@ -368,10 +403,12 @@ def bifocal_eq7_ref(q, k, v, pos, rope_base: float, remap_scale: int, window_lef
 
 def brute_force_prefill(q, k, v, pos, mode: str, rope_base: float, period: int = 0,
                         remap_scale: int = 1, window_left: int = -1,
-                        softmax_scale: Optional[float] = None, remote_map: str = "alias"):
+                        softmax_scale: Optional[float] = None, remote_map: str = "alias",
+                        alibi_slopes=None):
     """Pure-Python loops over (b, h, i, j, pair) with explicit 2x2 rotation blocks.
 
     For tiny inputs only. Returns O as nested float lists shaped [B][S][Hq][d].
+    ``alibi_slopes`` adds - m_h * (i - j) to each kept score (nope/rope).
     """
     q = np.asarray(q, dtype=np.float64).tolist()
     k = np.asarray(k, dtype=np.float64).tolist()
@@ -421,7 +458,8 @@ def brute_force_prefill(q, k, v, pos, mode: str, rope_base: float, period: int =
                         else:
                             ri, rj = pos[b][i] / remap_scale, pos[b][j] / remap_scale
                         s_ij = dot(block_rotate(q[b][i][h], ri), block_rotate(k[b][j][g], rj))
-                    scores.append(s_ij * scale)
+                    bias = 0.0 if alibi_slopes is None else -float(alibi_slopes[h]) * dist
+                    scores.append(s_ij * scale + bias)
                     idx.append(j)
                 mx = max(scores)
                 w = [math.exp(s - mx) for s in scores]

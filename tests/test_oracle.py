@@ -527,3 +527,231 @@ def test_interp_decode_equals_last_prefill_row(L, s, w0):
                                 window_left=w0, remote_map="interp")
     assert np.allclose(o_dec, o_pre[:, -1], atol=1e-10)
     assert np.allclose(l_dec, l_pre[:, :, -1], atol=1e-10)
+
+
+# ---------------------------------------------------------------- negative ids
+# Ids may be any integer: a negative id rotates backwards, the period takes the
+# mathematical remainder in [0, P) and the remote map the floor.
+
+def test_periodic_and_remote_index_of_negative_ids():
+    # P-RoPE Eq. (4) phi(t) = t mod W lies in [0, W); Jet-Long Eq. (3) is a floor
+    assert list(O.periodic_index([-1, -8, -9, 7], 8)) == [7, 0, 7, 7]
+    assert list(O.remote_index([-1, -2, -3, -4, -5, 5], 2)) == [-1, -1, -2, -2, -3, 2]
+
+
+def test_negative_shift_invariance_rope_and_bifocal():
+    # relative-offset property (P-RoPE Eq. (3)) for ids pushed below zero; for the
+    # bifocal map only shifts by a multiple of s keep floor(p / s) differences,
+    # which a truncating division of negative ids would break
+    q, k, v = _rand_qkv(1, 33, 2, 1, 16, 41)
+    pos = np.arange(33)[None]
+    o1, _ = O.prefill_ref(q, k, v, pos, "rope", rope_base=1e4)
+    o2, _ = O.prefill_ref(q, k, v, pos - 20, "rope", rope_base=1e4)
+    assert np.allclose(o1, o2, atol=1e-9)
+    p1, _ = O.prefill_ref(q, k, v, pos, "rope", rope_base=1e4, period=8, window_left=5)
+    p2, _ = O.prefill_ref(q, k, v, pos - 8 * 9, "rope", rope_base=1e4, period=8, window_left=5)
+    assert np.allclose(p1, p2, atol=1e-12)
+    kw = dict(rope_base=1e6, remap_scale=3, window_left=5)
+    b1, _ = O.prefill_ref(q, k, v, pos, "bifocal", **kw)
+    b2, _ = O.prefill_ref(q, k, v, pos - 3 * 7, "bifocal", **kw)
+    assert np.allclose(b1, b2, atol=1e-9)
+    trunc = pos - 3 * 7
+    # the same ids with a truncating division differ for the negative ones
+    assert np.any(np.trunc(trunc / 3) != O.remote_index(trunc, 3))
+
+
+def test_negative_ids_vectorized_equals_brute_force():
+    B, S, Hq, Hkv, d = 1, 10, 2, 1, 6
+    q, k, v = _rand_qkv(B, S, Hq, Hkv, d, 42)
+    pos = np.array([[-7, -6, -5, -3, -1, 0, 2, 4, -100, 9]])
+    for mode, kw in (("rope", dict(rope_base=1e4, period=4)), ("bifocal", dict(rope_base=1e4, remap_scale=3,
+                                                                                   window_left=2))):
+        o, _ = O.prefill_ref(q, k, v, pos, mode, **kw)
+        bf = np.array(O.brute_force_prefill(q, k, v, pos, mode, kw["rope_base"], period=kw.get("period", 0),
+                                            remap_scale=kw.get("remap_scale", 1),
+                                            window_left=kw.get("window_left", -1)))
+        assert np.allclose(o, bf, atol=1e-12), mode
+
+
+# ---------------------------------------------------------------- ALiBi on a sliding window
+# (P-RoPE page, section 1: SWA with ALiBi, the linear distance penalty clamped
+# to the window of W keys, with a manually set slope per head)
+
+def _alibi_mask(S, W, slopes):
+    """Additive float mask [H, S, S]: - m_h (i - j) on the W kept keys, -inf elsewhere."""
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    dist = i - j
+    kept = (dist >= 0) & ((dist <= W - 1) if W > 0 else True)
+    bias = -np.asarray(slopes, dtype=np.float64)[:, None, None] * dist[None]
+    return np.where(kept[None], bias, -np.inf)
+
+
+@pytest.mark.parametrize("W", [6, 0])
+def test_alibi_equals_sdpa_with_float_mask(W):
+    # W = 0: no window (global ALiBi over the causal keys)
+    B, S, Hq, Hkv, d = 1, 31, 4, 2, 8
+    q, k, v = _rand_qkv(B, S, Hq, Hkv, d, 43)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625])
+    pos = np.arange(S)[None]
+    o, _ = O.prefill_ref(q, k, v, pos, "nope", window_left=W - 1, alibi_slopes=slopes)
+    want = _sdpa(q, k, v, mask=_alibi_mask(S, W, slopes)[None])
+    assert np.allclose(o, want, atol=1e-12)
+    # rope on the same window: SDPA on inputs rotated by complex multiplication
+    base = 1e4
+    th = np.array([base ** (-(2 * i) / d) for i in range(d // 2)])
+
+    def crot(x):
+        z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * pos[:, :, None, None] * th)
+        y = np.empty_like(x)
+        y[..., 0::2], y[..., 1::2] = z.real, z.imag
+        return y
+
+    o_r, _ = O.prefill_ref(q, k, v, pos, "rope", rope_base=base, window_left=W - 1, alibi_slopes=slopes)
+    assert np.allclose(o_r, _sdpa(crot(q), crot(k), v, mask=_alibi_mask(S, W, slopes)[None]), atol=1e-12)
+
+
+def test_alibi_geometric_closed_form():
+    # q = 0: the logits of row i are - m * delta for delta = 0 .. n - 1 with
+    # n = min(i + 1, W) kept keys, so the weights are a geometric sequence r^delta,
+    # r = exp(-m): LSE = log((1 - r^n) / (1 - r)), and with v_j = (j, 1)
+    # O_i = i - sum(delta r^delta) / sum(r^delta)
+    #     = i - r (1 - n r^(n-1) + (n-1) r^n) / ((1 - r)(1 - r^n)).
+    S, W, m = 40, 11, 0.3
+    q = np.zeros((1, S, 1, 2))
+    k = _rng(44).standard_normal((1, S, 1, 2))
+    v = np.zeros((1, S, 1, 2))
+    v[0, :, 0, 0] = np.arange(S)
+    v[0, :, 0, 1] = 1.0
+    o, lse = O.prefill_ref(q, k, v, np.arange(S)[None], "nope", window_left=W - 1, alibi_slopes=[m])
+    r = math.exp(-m)
+    for i in range(S):
+        n = min(i + 1, W)
+        assert abs(lse[0, 0, i] - math.log((1 - r ** n) / (1 - r))) < 1e-12
+        mean_delta = r * (1 - n * r ** (n - 1) + (n - 1) * r ** n) / ((1 - r) * (1 - r ** n))
+        assert abs(o[0, i, 0, 0] - (i - mean_delta)) < 1e-11
+        assert abs(o[0, i, 0, 1] - 1.0) < 1e-13
+
+
+def test_alibi_zero_and_large_slopes():
+    q, k, v = _rand_qkv(1, 25, 2, 1, 8, 45)
+    pos = np.arange(25)[None]
+    plain, lp = O.prefill_ref(q, k, v, pos, "rope", rope_base=1e4, window_left=7)
+    zero, lz = O.prefill_ref(q, k, v, pos, "rope", rope_base=1e4, window_left=7, alibi_slopes=[0.0, 0.0])
+    assert np.array_equal(plain, zero) and np.array_equal(lp, lz)
+    # a steep slope leaves only the key at distance 0: O_i = v_i
+    big, _ = O.prefill_ref(q, k, v, pos, "rope", rope_base=1e4, window_left=7, alibi_slopes=[80.0, 80.0])
+    assert np.allclose(big[0, :, 0], v[0, :, 0], atol=1e-12)
+    assert np.allclose(big[0, :, 1], v[0, :, 0], atol=1e-12)
+
+
+@pytest.mark.parametrize("mode,kw", [
+    ("nope", dict(window_left=3)),
+    ("rope", dict(rope_base=1e4, period=5, window_left=4)),
+    ("rope", dict(rope_base=1e4)),
+])
+def test_alibi_vectorized_equals_brute_force(mode, kw):
+    B, S, Hq, Hkv, d = 2, 12, 4, 2, 6
+    q, k, v = _rand_qkv(B, S, Hq, Hkv, d, 46)
+    slopes = np.array([0.7, 0.2, 1.3, 0.05])
+    pos = np.stack([np.arange(S), np.concatenate([np.arange(6), np.arange(100, 106)])])
+    o, _ = O.prefill_ref(q, k, v, pos, mode, alibi_slopes=slopes, **kw)
+    bf = np.array(O.brute_force_prefill(q, k, v, pos, mode, kw.get("rope_base", 1e4), period=kw.get("period", 0),
+                                        window_left=kw.get("window_left", -1), alibi_slopes=slopes))
+    assert np.allclose(o, bf, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode,w", [("rope", 9), ("nope", -1)])
+def test_alibi_decode_equals_last_prefill_row(mode, w):
+    B, L, Hq, Hkv, d = 1, 30, 4, 2, 8
+    q, k, v = _rand_qkv(B, L, Hq, Hkv, d, 47)
+    slopes = np.array([0.4, 0.1, 0.9, 0.02])
+    pos = np.arange(L)[None]
+    kw = dict(rope_base=1e4) if mode == "rope" else {}
+    o_pre, l_pre = O.prefill_ref(q, k, v, pos, mode, window_left=w, alibi_slopes=slopes, **kw)
+    kc = O.rope_apply_ref(k, pos, 1e4) if mode == "rope" else k
+    ql = O.rope_apply_ref(q[:, -1:], pos[:, -1:], 1e4)[:, 0] if mode == "rope" else q[:, -1]
+    o_dec, l_dec = O.decode_ref(ql, kc, v, [L], mode, window_left=w, alibi_slopes=slopes)
+    assert np.allclose(o_dec, o_pre[:, -1], atol=1e-12)
+    assert np.allclose(l_dec, l_pre[:, :, -1], atol=1e-12)
+
+
+def test_alibi_rejected_for_bifocal():
+    q, k, v = _rand_qkv(1, 5, 1, 1, 4, 48)
+    with pytest.raises(ValueError):
+        O.prefill_ref(q, k, v, np.arange(5)[None], "bifocal", remap_scale=2, window_left=1, alibi_slopes=[0.1])
+
+
+# ---------------------------------------------------------------- real-valued interpolation scale
+# (Jet-Long page, section 3.1: s = max(1, L / w_pretrained) for continuous-style
+# rescaling; section 4.5: frequency interpolation as the remote map)
+
+def test_continuous_scale_values():
+    assert O.continuous_scale(10, 32) == 1.0
+    assert O.continuous_scale(32, 32) == 1.0
+    assert O.continuous_scale(48, 32) == 1.5
+    assert O.continuous_scale(131072, 32768) == 4.0
+    assert O.continuous_scale(100000, 32768) == 100000 / 32768
+    # the integer group size of Eq. (2) is its ceiling
+    for L in (1, 31, 32, 33, 100000):
+        assert O.group_size(L, 32) == math.ceil(O.continuous_scale(L, 32))
+
+
+@pytest.mark.parametrize("s", [1.5, 2.5, 131072 / 40000])
+def test_interp_real_scale_equals_sdpa_on_complex_rotation(s):
+    B, S, Hq, Hkv, d, base = 1, 27, 4, 2, 8, 1e6
+    q, k, v = _rand_qkv(B, S, Hq, Hkv, d, 49)
+    pos = np.arange(S)[None] * 5 + 3
+    th = np.array([base ** (-(2 * i) / d) for i in range(d // 2)]) / s
+
+    def crot(x):
+        z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * pos[:, :, None, None] * th)
+        y = np.empty_like(x)
+        y[..., 0::2], y[..., 1::2] = z.real, z.imag
+        return y
+
+    o, _ = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=base, remap_scale=s, window_left=-1,
+                         remote_map="interp")
+    assert np.allclose(o, _sdpa(crot(q), crot(k), v, causal=True), atol=1e-12)
+
+
+def test_interp_real_scale_brute_force_and_eq7():
+    B, S, Hq, Hkv, d = 1, 11, 2, 1, 6
+    q, k, v = _rand_qkv(B, S, Hq, Hkv, d, 50)
+    pos = np.arange(S)[None] + 3
+    o, _ = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=1e4, remap_scale=1.75, window_left=2,
+                         remote_map="interp")
+    bf = np.array(O.brute_force_prefill(q, k, v, pos, "bifocal", 1e4, remap_scale=1.75, window_left=2,
+                                        remote_map="interp"))
+    assert np.allclose(o, bf, atol=1e-12)
+    q2, k2, v2 = _rand_qkv(1, 48, 4, 2, 8, 51)
+    pos2 = np.arange(48)[None]
+    for w0, s in [(5, 1.5), (0, 2.25), (-1, 3.1), (47, 1.2)]:
+        direct, _ = O.prefill_ref(q2, k2, v2, pos2, "bifocal", rope_base=1e6, remap_scale=s, window_left=w0,
+                                  remote_map="interp")
+        eq7 = O.bifocal_eq7_ref(q2, k2, v2, pos2, rope_base=1e6, remap_scale=s, window_left=w0,
+                                remote_map="interp")
+        assert np.allclose(eq7, direct, atol=1e-10), (w0, s)
+
+
+@pytest.mark.parametrize("L,w_pre,w0", [(40, 16, 7), (33, 30, -1), (50, 64, 4)])
+def test_interp_continuous_decode_equals_last_prefill_row(L, w_pre, w0):
+    # the dynamic factor at the sequence's own length, s = max(1, L / w_pre)
+    s = O.continuous_scale(L, w_pre)
+    B, Hq, Hkv, d, base = 1, 4, 2, 16, 1e6
+    q, k, v = _rand_qkv(B, L, Hq, Hkv, d, 52)
+    pos = np.tile(np.arange(L), (B, 1))
+    o_pre, l_pre = O.prefill_ref(q, k, v, pos, "bifocal", rope_base=base, remap_scale=s, window_left=w0,
+                                 remote_map="interp")
+    kc = O.rope_apply_ref(k, pos, base)
+    ql = O.rope_apply_ref(q[:, -1:], pos[:, -1:], base)[:, 0]
+    o_dec, l_dec = O.decode_ref(ql, kc, v, np.full(B, L), "bifocal", rope_base=base, remap_scale=s,
+                                window_left=w0, remote_map="interp")
+    assert np.allclose(o_dec, o_pre[:, -1], atol=1e-10)
+    assert np.allclose(l_dec, l_pre[:, :, -1], atol=1e-10)
+
+
+def test_alias_rejects_real_scale():
+    q, k, v = _rand_qkv(1, 5, 1, 1, 4, 53)
+    with pytest.raises(ValueError):
+        O.prefill_ref(q, k, v, np.arange(5)[None], "bifocal", remap_scale=1.5, window_left=1)
