@@ -230,15 +230,29 @@ def bench_gemm(steps, warmup, n=8192):
     return dict(avg_ms=avg, tflops=2.0 * n ** 3 / (avg * 1e-3) / 1e12)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, n_rows: int):
-    """The fp64 oracle, as it stands, on a bounded sample of query rows of the same workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of query rows of the same workload.
+    Its matrix products run on the BLAS thread pool (the `cores` figure); its
+    elementwise steps (rotations, exp) on one thread."""
     import numpy as np
     import oracle as O
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads = affinity
     rng = np.random.default_rng(12345)
     rows = np.sort(rng.choice(w.S, size=n_rows, replace=False))
     q, k, v = (inp[n].double().numpy() for n in ("q", "k", "v"))
@@ -251,7 +265,7 @@ def cpu_baseline(w, inp, n_rows: int):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_rows} uniformly drawn query rows x all {w.Hq} heads of {w.name} "
                       f"({flops:.3e} algorithmic flop in {dt:.1f} s, fp64 NumPy)",
-            "seconds": dt}
+            "seconds": dt, "cpu_model": cpu_model(), "affinity_cpus": affinity, "blas_threads": int(threads)}
 
 
 def main():
@@ -262,7 +276,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K prefill and decode lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--only", choices=["prefill_64k", "prefill_128k", "prefill_64k_unfused", "decode_b1", "decode_b8", "copy"],
+    ap.add_argument("--only", choices=["prefill_64k", "prefill_128k", "prefill_64k_unfused", "prope_local_8k",
+                                       "nope_global_8k", "endprompt_fp32", "decode_b1", "decode_b8", "rope_apply",
+                                       "copy"],
                     help="time one leg only and print its figures (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -278,6 +294,12 @@ def main():
         if args.only == "copy":
             name = "copy_1GiB_fp32"
             r = bench_copy(args.steps, args.warmup)
+        elif args.only == "rope_apply":
+            name = "rope_apply_128k_k"
+            r = bench_rope_apply(args.steps, args.warmup)
+        elif args.only in ("prope_local_8k", "nope_global_8k", "endprompt_fp32"):
+            name = args.only
+            _, _, r = bench_prefill(name, args.steps, args.warmup, min_seconds=0.1)
         elif args.only.startswith("prefill"):
             name = "bifocal_128k" if args.only == "prefill_128k" else "bifocal_64k"
             _, _, r = bench_prefill(name, args.steps, args.warmup, unfused=args.only.endswith("unfused"))

@@ -9,6 +9,9 @@
  *     3.1 Eq. (1)-(3) and section 3.2 Eq. (4)-(5): rotate by p mod P) and
  *     optionally restricted to a causal sliding window; EndPrompt's
  *     two-segment ids are just an id array in this mode;
+ *   - the same on a sliding window with ALiBi biases (P-RoPE page, section 1:
+ *     SWA with ALiBi, a linear distance penalty clamped to the window, with a
+ *     manually set slope per head);
  *   - Jet-Long bifocal attention ("Jet-Long: Efficient Long-Context Extension
  *     with Dynamic Bifocal RoPE", section 3, Eq. (1)): keys within w0 of the
  *     query score with RoPE at the true ids, farther keys with RoPE at ids
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PROPE_VERSION 1
+#define PROPE_VERSION 2
 
 typedef enum {
   PROPE_OK = 0,
@@ -66,9 +69,10 @@ typedef enum {
 } prope_mode;
 
 typedef enum {
-  PROPE_REMOTE_ALIAS = 0,  /* remote ids floor(p / s) (Jet-Long Eq. (3))                   */
+  PROPE_REMOTE_ALIAS = 0,  /* remote ids floor(p / s) (Jet-Long Eq. (3)), integer s = G     */
   PROPE_REMOTE_INTERP = 1  /* remote angle p * theta_i / s: the frequency-interpolation
-                              mapping of Jet-Long section 4.5 (Table 6), unfloored        */
+                              mapping of Jet-Long section 4.5 (Table 6), unfloored; s may
+                              be any real number >= 1 (interp_scale)                      */
 } prope_remote_map;
 
 typedef struct {
@@ -81,14 +85,26 @@ typedef struct {
                             BIFOCAL: w0 >= -1, routing only; -1 = every key remote        */
   double rope_base;      /* Theta > 1 (e.g. 1e4, 1e6); ignored by NOPE                    */
   float softmax_scale;   /* > 0, or 0 for 1/sqrt(d)                                      */
-  int32_t w_pretrained;  /* 0: the remote scale is remap_scale. > 0 (BIFOCAL only, with
-                            remap_scale = 1): the dynamic group size of Jet-Long section
-                            3.1, Eq. (2), s = G(L) = max(1, ceil(L / w_pretrained)), with L
-                            the sequence length (prefill: S; decode: kv_len[b], per
-                            sequence, so a batch may straddle a boundary)              */
-  int32_t remote_map;    /* prope_remote_map; PROPE_REMOTE_INTERP is BIFOCAL only, and
-                            not with w_pretrained > 0 in decode or with the unfused call
-                            (PROPE_ERR_UNSUPPORTED)                                     */
+  int32_t w_pretrained;  /* 0: the remote scale is remap_scale (or interp_scale). > 0
+                            (BIFOCAL only, with remap_scale = 1 and interp_scale = 0): the
+                            scale follows the sequence length L (prefill: S; decode:
+                            kv_len[b], per sequence, so a batch may straddle a boundary),
+                            as Jet-Long section 3.1 gives it:
+                              PROPE_REMOTE_ALIAS:  the integer group size of Eq. (2),
+                                                   s = G(L) = max(1, ceil(L / w_pretrained));
+                              PROPE_REMOTE_INTERP: the continuous-style factor
+                                                   s = max(1, L / w_pretrained)          */
+  int32_t remote_map;    /* prope_remote_map; PROPE_REMOTE_INTERP is BIFOCAL only        */
+  int32_t reserved;      /* must be 0                                                    */
+  double interp_scale;   /* PROPE_REMOTE_INTERP only: the real scale s >= 1 (finite), with
+                            remap_scale = 1 and w_pretrained = 0; 0 = use remap_scale    */
+  const float* alibi_slopes; /* NULL, or a DEVICE array of Hq float32 slopes m_h (NOPE and
+                            ROPE modes only): each kept key's scaled score gets
+                            - m_h * (i - j) added (decode: - m_h * (kv_len - 1 - j)). With
+                            window_left >= 0 the window masks every key beyond it, which
+                            clamps the penalty to distances 0 .. window_left as in the
+                            P-RoPE page's SWA + ALiBi layer. Read by the kernels, so it
+                            must stay valid until the call's work has run.              */
 } prope_params;
 
 /*
@@ -97,7 +113,9 @@ typedef struct {
  *     q and k UNROTATED (rotation is fused into the kernel's tile loads).
  *   lse [B,Hq,S] float32, natural-log log-sum-exp of each row's kept scaled
  *     scores; may be NULL.
- *   pos [B,S] int32 position ids, each >= 0 (NOPE: ignored, may be NULL).
+ *   pos [B,S] int32 position ids, any value (NOPE: ignored, may be NULL). A
+ *     negative id rotates backwards; the period takes p mod P in [0, P) and the
+ *     remote map floor(p / s), both with mathematical (floor) semantics.
  *   Query head h reads KV head h / (Hq / Hkv); Hq % Hkv must be 0.
  *   d in {64, 128}; 1 <= S; 1 <= B; bf16 or fp32. One sequence's q slice
  *   (S * Hq * d elements) must stay under 2^30 elements (32-bit byte offsets),
@@ -146,7 +164,8 @@ int prope_attn_prefill_queued(const void* q, const void* k, const void* v, void*
  * rounds its O_X to dt); provided to measure the fused kernel against the
  * construction it replaces and to check Eq. (7) on the device.
  *   Arguments as prope_attn_prefill; params->mode must be PROPE_BIFOCAL and
- *   pos is required (ids >= 0).
+ *   pos is required. With PROPE_REMOTE_INTERP, B and C rotate at the ids pos
+ *   with the interpolated frequencies theta_i / s instead of at floor(pos / s).
  *   workspace: caller-owned device buffer, 256-byte aligned, of at least
  *     prope_bifocal_unfused_workspace_size(B, S, Hq, d, dt) bytes (O_A, O_C,
  *     three LSE vectors, remote ids, and the work queue of the three calls,
@@ -177,8 +196,11 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
  *   BIFOCAL: keys with (kv_len-1) - j <= w0 score q.k; farther keys score
  *     RoPE(q, dq).RoPE(k_j, dk_j) with dq = floor(p_q/s) - p_q and
  *     dk_j = floor(j/s) - j (Jet-Long Eq. (5)-(6)), computed in registers.
+ *   With PROPE_REMOTE_INTERP the corrections are p_q * (theta_i / s - theta_i)
+ *     and j * (theta_i / s - theta_i); with w_pretrained > 0, s = max(1,
+ *     kv_len[b] / w_pretrained) per sequence.
  *   NOPE/ROPE: scores q.k_j (q and cache already carry the layer's rotation),
- *     keys beyond window_left masked. `period` must be 0.
+ *     keys beyond window_left masked, optional ALiBi biases. `period` must be 0.
  *   workspace: caller-owned device buffer of at least
  *     prope_decode_workspace_size(B, Lmax, Hq, d) bytes (split-K partials);
  *     too small -> PROPE_ERR_WORKSPACE. bf16 only; Hq / Hkv <= 16, B and

@@ -41,7 +41,9 @@ class PropeParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("period", ctypes.c_int32),
                 ("remap_scale", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("w_pretrained", ctypes.c_int32), ("remote_map", ctypes.c_int32)]
+                ("w_pretrained", ctypes.c_int32), ("remote_map", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("interp_scale", ctypes.c_double),
+                ("alibi_slopes", ctypes.c_void_p)]
 
 
 _lib = None
@@ -97,11 +99,12 @@ def _check(code: int):
 
 
 def _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained=0,
-            remote_map="alias") -> PropeParams:
+            remote_map="alias", interp_scale=0.0, alibi_slopes=None) -> PropeParams:
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
     r = _REMOTE[remote_map] if isinstance(remote_map, str) else int(remote_map)
     return PropeParams(m, int(period), int(remap_scale), int(window_left), float(rope_base),
-                       float(softmax_scale), int(w_pretrained), r)
+                       float(softmax_scale), int(w_pretrained), r, 0, float(interp_scale),
+                       _ptr(alibi_slopes))
 
 
 def _dtype_code(t) -> int:
@@ -131,18 +134,46 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _like(t, name, shape, dtype, device):
+    """Check a caller-supplied output tensor: the C ABI cannot see buffer sizes."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise PropeError(f"{name} must be {dtype} {list(shape)} on {device}, "
+                         f"not {t.dtype} {list(t.shape)} on {t.device}")
+
+
+def _slopes(alibi_slopes, Hq, device):
+    import torch
+    if alibi_slopes is None:
+        return None
+    _dev(alibi_slopes, "alibi_slopes")
+    _like(alibi_slopes, "alibi_slopes", (Hq,), torch.float32, device)
+    return alibi_slopes
+
+
 # Work-queue buffers of the queued prefill, one per (device, stream): calls on
 # one stream run in order and each leaves its queue zero for the next.
 _queues = {}
 
 
 def prefill_queue(device, stream: int):
-    """The zero-filled work-queue buffer of prope_attn_prefill_queued for this (device, stream)."""
+    """The zero-filled work-queue buffer of prope_attn_prefill_queued for this (device, stream).
+
+    Under HIP graph capture every call gets a buffer of its own, allocated (and
+    zero-filled by a captured fill kernel) inside the capture: graphs captured on
+    one stream may be replayed in any order or at the same time, so they must not
+    share counters, and a cached buffer first created inside a capture would only
+    be zeroed when the graph replays.
+    """
     import torch
+    n = int(lib().prope_prefill_queue_size())
+    if torch.cuda.is_current_stream_capturing():
+        return torch.zeros(n, dtype=torch.uint8, device=device)
     key = (torch.device(device).index, int(stream))
     buf = _queues.get(key)
     if buf is None:
-        buf = torch.zeros(int(lib().prope_prefill_queue_size()), dtype=torch.uint8, device=device)
+        buf = torch.zeros(n, dtype=torch.uint8, device=device)
         _queues[key] = buf
     return buf
 
@@ -162,6 +193,9 @@ def rope_apply(x, pos, rope_base: float, out=None):
     _dev(x, "x"); _dev(pos, "pos")
     if pos.dtype != torch.int32 or x.dim() != 4 or tuple(pos.shape) != tuple(x.shape[:2]):
         raise PropeError("x must be [B,S,H,d] and pos int32 [B,S]")
+    if pos.device != x.device:
+        raise PropeError(f"pos must be on {x.device}")
+    _like(out, "out", x.shape, x.dtype, x.device)
     y = torch.empty_like(x) if out is None else out
     _dev(y, "out")
     B, S, H, d = x.shape
@@ -173,10 +207,12 @@ def rope_apply(x, pos, rope_base: float, out=None):
 def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
             remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
             out=None, lse=None, return_lse: bool = False, w_pretrained: int = 0, remote_map="alias",
-            schedule: str = "queue"):
+            schedule: str = "queue", interp_scale: float = 0.0, alibi_slopes=None):
     """Causal attention with RoPE fused under remapped ids (see include/prope.h).
 
     q [B,S,Hq,d], k/v [B,S,Hkv,d] unrotated; pos int32 [B,S] (None for NoPE).
+    interp_scale: real remote scale s >= 1 of the interpolation map.
+    alibi_slopes: float32 [Hq] device tensor of ALiBi slopes (nope/rope modes).
     schedule "queue" calls prope_attn_prefill_queued with this stream's queue
     buffer, "static" calls prope_attn_prefill; both give the same bits.
     Returns O [B,S,Hq,d] (and LSE float32 [B,Hq,S] if return_lse).
@@ -191,10 +227,17 @@ def prefill(q, k, v, pos, mode="rope", rope_base: float = 1e4, period: int = 0,
         raise PropeError("k and v must be [B,S,Hkv,d] with q's dtype")
     if pos is not None and (pos.dtype != torch.int32 or tuple(pos.shape) != (B, S)):
         raise PropeError("pos must be int32 [B,S]")
+    for t, n in ((k, "k"), (v, "v"), (pos, "pos")):
+        if t is not None and t.device != q.device:
+            raise PropeError(f"{n} must be on {q.device}")
+    _like(out, "out", q.shape, q.dtype, q.device)
+    _like(lse, "lse", (B, Hq, S), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained, remote_map)
+    slopes = _slopes(alibi_slopes, Hq, q.device)
+    p = _params(mode, rope_base, period, remap_scale, window_left, softmax_scale, w_pretrained, remote_map,
+                interp_scale, slopes)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos), B, S, Hq, Hkv, d, _dtype_code(q),
             ctypes.byref(p))
     st = _stream(q)
@@ -213,7 +256,8 @@ def bifocal_unfused_workspace_size(B: int, S: int, Hq: int, d: int, dtype_code: 
 
 def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: int = 1, window_left: int = -1,
                             softmax_scale: float = 0.0, out=None, lse=None, workspace=None,
-                            return_lse: bool = False, w_pretrained: int = 0):
+                            return_lse: bool = False, w_pretrained: int = 0, remote_map="alias",
+                            interp_scale: float = 0.0):
     """Bifocal prefill as three attention calls merged by Jet-Long Eq. (7) (see include/prope.h)."""
     import torch
     L = lib()
@@ -225,13 +269,19 @@ def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: i
         raise PropeError("k and v must be [B,S,Hkv,d] with q's dtype")
     if pos is None or pos.dtype != torch.int32 or tuple(pos.shape) != (B, S):
         raise PropeError("pos must be int32 [B,S]")
+    for t, n in ((k, "k"), (v, "v"), (pos, "pos"), (workspace, "workspace")):
+        if t is not None and t.device != q.device:
+            raise PropeError(f"{n} must be on {q.device}")
+    _like(out, "out", q.shape, q.dtype, q.device)
+    _like(lse, "lse", (B, Hq, S), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     need = L.prope_bifocal_unfused_workspace_size(B, S, Hq, d, _dtype_code(q))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    p = _params("bifocal", rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained)
+    p = _params("bifocal", rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained, remote_map,
+                interp_scale)
     _check(L.prope_attn_prefill_bifocal_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(pos),
                                                 B, S, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p),
                                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -242,7 +292,7 @@ def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: i
 def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
            remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
            out=None, lse=None, workspace=None, return_lse: bool = False, w_pretrained: int = 0,
-           remote_map="alias"):
+           remote_map="alias", interp_scale: float = 0.0, alibi_slopes=None):
     """One decode step: q [B,Hq,d] base-rotated, caches [B,Lmax,Hkv,d], kv_len int32 [B]."""
     import torch
     L = lib()
@@ -253,15 +303,24 @@ def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
     if k_cache.shape != (B, Lmax, Hkv, d) or v_cache.shape != k_cache.shape:
         raise PropeError("caches must be [B,Lmax,Hkv,d]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise PropeError("k_cache and v_cache must have q's dtype")
     if kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,):
         raise PropeError("kv_len must be int32 [B]")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (kv_len, "kv_len"), (workspace, "workspace")):
+        if t is not None and t.device != q.device:
+            raise PropeError(f"{n} must be on {q.device}")
+    _like(out, "out", q.shape, q.dtype, q.device)
+    _like(lse, "lse", (B, Hq), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     need = L.prope_decode_workspace_size(B, Lmax, Hq, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    p = _params(mode, rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained, remote_map)
+    slopes = _slopes(alibi_slopes, Hq, q.device)
+    p = _params(mode, rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained, remote_map,
+                interp_scale, slopes)
     _check(L.prope_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
                                _ptr(kv_len), B, Lmax, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -12,7 +12,7 @@
 
 namespace prope {
 
-void fill_rope_freq(RopeFreq& f, int d, double base, int s) {
+void fill_rope_freq(RopeFreq& f, int d, double base, long double s) {
   // F_i = round(theta_i / (2 pi s) * 2^64), theta_i = base^(-2i/d) (P-RoPE page, Eq. (1));
   // s > 1 gives the interpolated frequencies theta_i / s. theta_i is the running
   // product of base^(-2/d) in long double (one powl per call instead of one per
@@ -46,10 +46,18 @@ bool valid_base(double b) { return isfinite(b) && b > 1.0; }
 // cache already carries the layer's rotation).
 int check_params(const prope_params* p, bool decode) {
   if (!p) return PROPE_ERR_INVALID_ARG;
+  if (p->reserved != 0) return PROPE_ERR_INVALID_ARG;
   if (p->w_pretrained < 0) return PROPE_ERR_INVALID_ARG;
   if (p->remote_map != PROPE_REMOTE_ALIAS && p->remote_map != PROPE_REMOTE_INTERP) return PROPE_ERR_INVALID_ARG;
   if (p->remote_map == PROPE_REMOTE_INTERP && p->mode != PROPE_BIFOCAL) return PROPE_ERR_INVALID_ARG;
   if (p->w_pretrained > 0 && (p->mode != PROPE_BIFOCAL || p->remap_scale != 1)) return PROPE_ERR_INVALID_ARG;
+  // a real interpolation scale: finite, >= 1, and the only source of s
+  if (!(p->interp_scale == 0.0 || (isfinite(p->interp_scale) && p->interp_scale >= 1.0))) return PROPE_ERR_INVALID_ARG;
+  if (p->interp_scale != 0.0 &&
+      (p->remote_map != PROPE_REMOTE_INTERP || p->remap_scale != 1 || p->w_pretrained != 0))
+    return PROPE_ERR_INVALID_ARG;
+  // ALiBi biases belong to the nope/rope layers (P-RoPE page, section 1)
+  if (p->alibi_slopes && p->mode == PROPE_BIFOCAL) return PROPE_ERR_INVALID_ARG;
   if (p->mode != PROPE_NOPE && p->mode != PROPE_ROPE && p->mode != PROPE_BIFOCAL)
     return PROPE_ERR_INVALID_ARG;
   if (p->period < 0 || p->remap_scale < 1 || p->window_left < -1) return PROPE_ERR_INVALID_ARG;
@@ -60,12 +68,24 @@ int check_params(const prope_params* p, bool decode) {
   return PROPE_OK;
 }
 
-// The remote scale s for a sequence of length L: remap_scale, or the dynamic
+// The aliasing scale s for a sequence of length L: remap_scale, or the dynamic
 // group size of Jet-Long Eq. (2) when w_pretrained > 0.
 int remote_scale(const prope_params& p, int64_t L) {
   if (p.w_pretrained <= 0) return p.remap_scale;
   const int64_t g = (L + p.w_pretrained - 1) / p.w_pretrained;
   return g < 1 ? 1 : static_cast<int>(g);
+}
+
+// The interpolation scale s for a sequence of length L: interp_scale, else the
+// continuous-style factor max(1, L / w_pretrained) of Jet-Long section 3.1 when
+// w_pretrained > 0, else the integer remap_scale.
+long double interp_scale(const prope_params& p, int64_t L) {
+  if (p.interp_scale > 0.0) return p.interp_scale;
+  if (p.w_pretrained > 0) {
+    const long double s = static_cast<long double>(L) / p.w_pretrained;
+    return s > 1.0L ? s : 1.0L;
+  }
+  return p.remap_scale;
 }
 
 float scale_log2(const prope_params* p, int d) {
@@ -125,8 +145,11 @@ int device_cus() {
   return n_cu;
 }
 
+// `freq_scale` divides the base frequencies (theta_i / freq_scale): the remote
+// calls of the unfused composition with the interpolation map.
 PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* pos,
-                         int B, int S, int Hq, int Hkv, int d, const prope_params& p, uint32_t* queue = nullptr) {
+                         int B, int S, int Hq, int Hkv, int d, const prope_params& p, uint32_t* queue = nullptr,
+                         long double freq_scale = 1.0L) {
   PrefillArgs a{};
   a.queue = queue;
   a.n_cu = queue ? device_cus() : 0;
@@ -141,13 +164,13 @@ PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, f
   a.period = p.period;
   a.window_left = p.window_left;
   a.period_div = make_fastdiv(p.period > 0 ? static_cast<uint32_t>(p.period) : 1u);
-  const int s = remote_scale(p, S);
   const bool interp = p.remote_map == PROPE_REMOTE_INTERP;
-  a.scale_div = make_fastdiv(static_cast<uint32_t>(interp ? 1 : s));
+  a.scale_div = make_fastdiv(static_cast<uint32_t>(interp ? 1 : remote_scale(p, S)));
   a.scale_log2 = scale_log2(&p, d);
-  fill_rope_freq(a.f, d, p.mode == PROPE_NOPE ? 10000.0 : p.rope_base);
+  a.alibi = p.alibi_slopes;
+  fill_rope_freq(a.f, d, p.mode == PROPE_NOPE ? 10000.0 : p.rope_base, freq_scale);
   if (interp)
-    fill_rope_freq(a.fr, d, p.rope_base, s);
+    fill_rope_freq(a.fr, d, p.rope_base, interp_scale(p, S));
   else
     a.fr = a.f;
   return a;
@@ -267,7 +290,6 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
   const int pc = check_prefill(q, k, v, o, pos, B, S, Hq, Hkv, d, dt, params);
   if (pc != PROPE_OK) return pc;
   if (params->mode != PROPE_BIFOCAL || !pos || !workspace) return PROPE_ERR_INVALID_ARG;
-  if (params->remote_map != PROPE_REMOTE_ALIAS) return PROPE_ERR_UNSUPPORTED;  // the calls take integer ids
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return PROPE_ERR_INVALID_ARG;
   const UnfusedLayout ly = unfused_layout(B, S, Hq, d, dt);
   if (workspace_bytes < ly.total) return PROPE_ERR_WORKSPACE;
@@ -288,27 +310,34 @@ int prope_attn_prefill_bifocal_unfused(const void* q, const void* k, const void*
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int w0 = params->window_left;
 
-  // the three calls are plain RoPE attention (no period) on two id arrays
+  // The three calls are plain RoPE attention (no period). The remote view
+  // (B, C) is RoPE at the ids floor(pos / s) (aliasing), or at the ids pos
+  // with the frequencies theta_i / s (interpolation).
   prope_params call = *params;
   call.mode = PROPE_ROPE;
   call.remap_scale = 1;
   call.period = 0;
   call.w_pretrained = 0;
-  if (launch_remap_ids(pos, rid, int64_t(B) * S, make_fastdiv(static_cast<uint32_t>(remote_scale(*params, S))),
-                       st) != hipSuccess)
+  call.remote_map = PROPE_REMOTE_ALIAS;
+  call.interp_scale = 0.0;
+  const bool interp = params->remote_map == PROPE_REMOTE_INTERP;
+  const long double rscale = interp ? interp_scale(*params, S) : 1.0L;
+  const int32_t* rpos = interp ? pos : rid;
+  if (!interp && launch_remap_ids(pos, rid, int64_t(B) * S,
+                                  make_fastdiv(static_cast<uint32_t>(remote_scale(*params, S))), st) != hipSuccess)
     return PROPE_ERR_HIP;
   if (wq && launch_zero_words(wq, kQueueWords, st) != hipSuccess) return PROPE_ERR_HIP;
-  // B: full causal attention at the remote ids, written straight into o
+  // B: full causal attention in the remote view, written straight into o
   call.window_left = -1;
-  int rc = run_prefill(prefill_args(q, k, v, o, lb, rid, B, S, Hq, Hkv, d, call, wq), dt, stream);
+  int rc = run_prefill(prefill_args(q, k, v, o, lb, rpos, B, S, Hq, Hkv, d, call, wq, rscale), dt, stream);
   if (rc != PROPE_OK) return rc;
   const bool windows = w0 >= 0;  // w0 = -1: no local window, the result is B alone
   if (windows) {
-    // A: the local window at the ids themselves; C: the local window at the remote ids
+    // A: the local window at the ids themselves; C: the local window in the remote view
     call.window_left = w0;
     rc = run_prefill(prefill_args(q, k, v, oa, la, pos, B, S, Hq, Hkv, d, call, wq), dt, stream);
     if (rc != PROPE_OK) return rc;
-    rc = run_prefill(prefill_args(q, k, v, oc, lc, rid, B, S, Hq, Hkv, d, call, wq), dt, stream);
+    rc = run_prefill(prefill_args(q, k, v, oc, lc, rpos, B, S, Hq, Hkv, d, call, wq, rscale), dt, stream);
     if (rc != PROPE_OK) return rc;
   }
   return launch_eq7_merge(oa, la, o, lb, oc, lc, lse, B, S, Hq, d, dt, windows, st) == hipSuccess ? PROPE_OK
@@ -338,7 +367,6 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
        reinterpret_cast<uintptr_t>(workspace)) % 16)
     return PROPE_ERR_INVALID_ARG;
   const bool interp = params->remote_map == PROPE_REMOTE_INTERP;
-  if (interp && params->w_pretrained > 0) return PROPE_ERR_UNSUPPORTED;  // per-sequence frequency tables
   if (workspace_bytes < prope_decode_workspace_size(B, Lmax, Hq, d)) return PROPE_ERR_WORKSPACE;
   // one sequence's cache slice is addressed with 32-bit byte offsets
   if (int64_t(Lmax) * Hkv * d * 2 >= (int64_t(1) << 32)) return PROPE_ERR_UNSUPPORTED;
@@ -369,11 +397,14 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
   a.scale_div = make_fastdiv(static_cast<uint32_t>(interp ? 1 : params->remap_scale));
   a.w_pre = params->w_pretrained;
   a.scale_log2 = scale_log2(params, d);
+  a.alibi = params->alibi_slopes;
   fill_rope_freq(a.f, d, params->mode == PROPE_NOPE ? 10000.0 : params->rope_base);
   a.interp = interp;
-  if (interp) {  // correction frequencies theta_i / s - theta_i, modulo one turn
+  if (interp && a.w_pre > 0) {
+    a.fr = a.f;  // per sequence: the kernel forms theta_i / s - theta_i from f and kv_len
+  } else if (interp) {  // correction frequencies theta_i / s - theta_i, modulo one turn
     RopeFreq fs;
-    fill_rope_freq(fs, d, params->rope_base, params->remap_scale);
+    fill_rope_freq(fs, d, params->rope_base, interp_scale(*params, Lmax));
     for (int i = 0; i < kMaxPairs; ++i) {
       const uint64_t c = ((uint64_t(fs.hi[i]) << 32) | fs.lo[i]) - ((uint64_t(a.f.hi[i]) << 32) | a.f.lo[i]);
       a.fr.lo[i] = static_cast<uint32_t>(c);

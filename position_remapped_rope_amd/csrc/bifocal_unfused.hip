@@ -11,7 +11,9 @@
 // score the window keys identically, so W_B O_B - W_C O_C keeps only the
 // remote keys (the inclusion-exclusion step).
 //
-// remap_ids_kernel writes floor(p / s) for the remote calls; eq7_merge_kernel
+// remap_ids_kernel writes floor(p / s) (any sign) for the remote calls of the
+// aliasing map; with the interpolation map the remote calls rotate at the ids
+// themselves with frequencies theta_i / s. eq7_merge_kernel
 // is a streaming pass over the three outputs (HBM-bound: it reads three rows
 // of d values and writes one per (token, query head)).
 #include "internal.hpp"
@@ -22,7 +24,7 @@ namespace {
 __global__ __launch_bounds__(256) void remap_ids_kernel(const int32_t* __restrict__ pos, int32_t* __restrict__ out,
                                                         int64_t n, FastDiv s) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = static_cast<int32_t>(fastdiv(static_cast<uint32_t>(pos[i]), s));
+  if (i < n) out[i] = floordiv_s(pos[i], s);
 }
 
 // clears the prefill work queue that the three calls share (vector stores)

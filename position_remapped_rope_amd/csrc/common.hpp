@@ -24,17 +24,12 @@ struct RopeFreq {
 };
 
 // Top 32 bits of (r * F) mod 2^64: the phase in units of 2^-32 turn. Works for
-// negative r (two's complement sign extension of r to 64 bits).
+// negative r (two's complement sign extension of r to 64 bits: the unsigned
+// product of r + 2^32 carries an extra 2^32 * F, whose top half is flo).
 __device__ __forceinline__ uint32_t phase_top(int32_t r, uint32_t flo, uint32_t fhi) {
   const uint32_t ru = static_cast<uint32_t>(r);
-  uint32_t top = __umulhi(ru, flo) + ru * fhi;
-  if (r < 0) top -= flo;
-  return top;
-}
-
-// The same for r >= 0 (prefill ids): no sign correction.
-__device__ __forceinline__ uint32_t phase_top_u(uint32_t r, uint32_t flo, uint32_t fhi) {
-  return __umulhi(r, flo) + r * fhi;
+  const uint32_t sgn = static_cast<uint32_t>(r >> 31);  // all ones iff r < 0
+  return __umulhi(ru, flo) + ru * fhi - (flo & sgn);
 }
 
 // sin and cos of 2*pi*t for t in [-1/2, 1/2) (v_sin_f32 / v_cos_f32 take revolutions).
@@ -111,6 +106,29 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv& f) {
 
 __host__ __device__ inline uint32_t fastmod(uint32_t n, const FastDiv& f) {
   return n - fastdiv(n, f) * f.div;
+}
+
+// floor(n / d) for any int32 n: for n < 0 the complement ~n = -n - 1 is in
+// [0, 2^31), and floor(n / d) = ~floor(~n / d).
+__host__ __device__ inline int32_t floordiv_s(int32_t n, const FastDiv& f) {
+  const uint32_t sgn = static_cast<uint32_t>(n >> 31);
+  return static_cast<int32_t>(fastdiv(static_cast<uint32_t>(n) ^ sgn, f) ^ sgn);
+}
+
+// n mod d in [0, d) for any int32 n (the remainder of the floor division; formed
+// modulo 2^32, where n - floor(n/d) * d cannot overflow)
+__host__ __device__ inline int32_t floormod_s(int32_t n, const FastDiv& f) {
+  return static_cast<int32_t>(static_cast<uint32_t>(n) - static_cast<uint32_t>(floordiv_s(n, f)) * f.div);
+}
+
+// floor(F * num / den) for 64-bit F and 0 < num <= den < 2^31 (so the quotient
+// fits in 64 bits): schoolbook division of the 96-bit product by 32-bit limbs.
+__host__ __device__ inline uint64_t muldiv_u64(uint64_t F, uint32_t num, uint32_t den) {
+  const uint64_t lo = (F & 0xffffffffull) * num;
+  const uint64_t hi = (F >> 32) * num + (lo >> 32);  // < 2^63 + 2^32
+  const uint64_t q1 = hi / den, r1 = hi % den;
+  const uint64_t q0 = ((r1 << 32) | (lo & 0xffffffffull)) / den;
+  return (q1 << 32) + q0;
 }
 
 // ---- XCD-aware work order ---------------------------------------------

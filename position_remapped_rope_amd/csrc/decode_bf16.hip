@@ -7,8 +7,13 @@
 // dq = floor(p_q/s) - p_q and dk_j = floor(j/s) - j (Eq. (5)-(6)); with the
 // frequency-interpolation mapping (same page, section 4.5) the corrections are
 // p_q * (theta_i/s - theta_i) and j * (theta_i/s - theta_i). Both are formed in
-// registers from exact integer phases; nothing is written back. NOPE/ROPE caches already carry their rotation, so those modes
-// score q . k_j with an optional window.
+// registers from exact integer phases; nothing is written back. With the
+// interpolation map and a per-sequence scale s = max(1, kv_len / w_pre) (the
+// continuous-style factor of Jet-Long section 3.1), each workgroup forms the
+// correction frequencies theta_i * w_pre / kv_len - theta_i from the exact
+// 64-bit phases. NOPE/ROPE caches already carry their rotation, so those modes
+// score q . k_j with an optional window and optional ALiBi biases
+// - m_h (p_q - j) (P-RoPE page, section 1).
 //
 // Kernel 1 (split): one workgroup per (chunk of a.chunk keys, group of a.hpw
 // KV heads, sequence). With hpw = 4 each of its 4 waves streams the whole chunk
@@ -106,11 +111,18 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const int b = blockIdx.z;
   const int kl = lane & 15, kg = lane >> 4;
   const int G = a.G;
-  if (MODE == kBifocal) {  // frequency table of the exact per-key phases (all waves, before any exit)
-    if (tid < D / 2) ftab[tid] = make_uint2(a.fr.lo[tid], a.fr.hi[tid]);
+  const int L = min(max(a.kv_len[b], 0), a.Lmax);  // a length outside [0, Lmax] never reads past the cache
+  if (MODE == kBifocal) {  // correction frequencies of the query and key phases (all waves, before any exit)
+    if (tid < D / 2) {
+      uint64_t c = (uint64_t(a.fr.hi[tid]) << 32) | a.fr.lo[tid];
+      if (a.interp && a.w_pre > 0) {  // theta_i / s - theta_i with s = L / w_pre when L > w_pre, else 0
+        const uint64_t F = (uint64_t(a.f.hi[tid]) << 32) | a.f.lo[tid];
+        c = L > a.w_pre ? muldiv_u64(F, static_cast<uint32_t>(a.w_pre), static_cast<uint32_t>(L)) - F : 0;
+      }
+      ftab[tid] = make_uint2(static_cast<uint32_t>(c), static_cast<uint32_t>(c >> 32));
+    }
     __syncthreads();
   }
-  const int L = min(max(a.kv_len[b], 0), a.Lmax);  // a length outside [0, Lmax] never reads past the cache
   const int jbeg = chunk * a.chunk;
   const size_t head_stride = size_t(a.n_chunks) * (D + 2);
   float* wsb = a.ws + (size_t(b) * a.Hq + size_t(kvh) * G) * head_stride + size_t(chunk) * (D + 2);
@@ -126,6 +138,9 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const int pq = L - 1;
   const float sl2 = a.scale_log2;
   const int w0 = a.window_left;
+  // ALiBi slope of this lane's head kl, log2 units (0: no bias)
+  const float slope2 =
+      (MODE != kBifocal && a.alibi && kl < G) ? a.alibi[size_t(kvh) * G + kl] * 1.4426950408889634f : 0.f;
 
   // ---- query operand (B of S^T = K Q^T): lane l holds head kl, dims 8kg + 32ks .. +7
   // in the local view (as given) and the remote view RoPE(q, dq), both bf16.
@@ -151,7 +166,8 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
       for (int e = 0; e < 4; ++e) {
         const int pi = 4 * kg + 16 * ks + e;
         float sn, cs, y0, y1;
-        rope_sincos(dq, a.fr.lo[pi], a.fr.hi[pi], sn, cs);
+        const uint2 fq = ftab[pi];
+        rope_sincos(dq, fq.x, fq.y, sn, cs);
         rot_pair(bf16_lo(w[e]), bf16_hi(w[e]), cs, sn, y0, y1);
         y[e] = pack_bf16(y0, y1);
       }
@@ -179,9 +195,9 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int pi = 4 * kg + 16 * ks + e;
-        ph[ks][e] = phase_top(dk0, a.fr.lo[pi], a.fr.hi[pi]);
-        inc[ks][e] = phase_top(d16, a.fr.lo[pi], a.fr.hi[pi]);
+        const uint2 fk = ftab[4 * kg + 16 * ks + e];
+        ph[ks][e] = phase_top(dk0, fk.x, fk.y);
+        inc[ks][e] = phase_top(d16, fk.x, fk.y);
       }
   }
 
@@ -277,7 +293,8 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
         else
           v = sloc[i];
         const bool keep = j < wend && (MODE == kBifocal || w0 < 0 || dist <= w0);
-        sc[blk][i] = keep ? v * sl2 : -INFINITY;
+        const float bias = MODE == kBifocal ? 0.f : -slope2 * static_cast<float>(dist);
+        sc[blk][i] = keep ? fmaf(v, sl2, bias) : -INFINITY;
       }
       if (more) load_k(j0 + kStep, blk);
     }

@@ -32,6 +32,7 @@ struct PrefillArgs {
   float scale_log2;   // softmax scale * log2(e)
   RopeFreq f;         // theta_i at the base ids
   RopeFreq fr;        // theta_i at the remote ids: theta_i (alias) or theta_i / s
+  const float* alibi; // NOPE/ROPE: Hq ALiBi slopes (device), or nullptr
   uint32_t* queue;    // bf16: work-queue counters (kQueueWords), or nullptr: one item per workgroup
   int n_cu;           // compute units of the device (persistent grid size with a queue)
 };
@@ -58,16 +59,20 @@ struct DecodeArgs {
   int mode;
   int window_left;
   FastDiv scale_div;  // remote scale s (alias, w_pre == 0)
-  int w_pre;          // > 0: s = max(1, ceil(kv_len / w_pre)) per sequence (alias only)
+  int w_pre;          // > 0: per-sequence scale from kv_len: alias s = max(1, ceil(kv_len / w_pre));
+                      // interpolation s = max(1, kv_len / w_pre), whose correction
+                      // frequencies the kernel forms from f
   int interp;         // remote angles p * theta_i / s instead of floor(p / s) * theta_i
   float scale_log2;
+  const float* alibi; // NOPE/ROPE: Hq ALiBi slopes (device), or nullptr
   RopeFreq f;         // theta_i
   RopeFreq fr;        // correction frequencies: theta_i (alias, index floor(p/s) - p) or
-                      // theta_i / s - theta_i (interpolation, index p)
+                      // theta_i / s - theta_i (interpolation, index p; unused with w_pre > 0)
 };
 
-// Fill F_i = round(theta_i / (2 pi s) * 2^64), theta_i = base^(-2i/d), in long double.
-void fill_rope_freq(RopeFreq& f, int d, double base, int s = 1);
+// Fill F_i = round(theta_i / (2 pi s) * 2^64), theta_i = base^(-2i/d), in long double
+// (s >= 1 real: the interpolated frequencies theta_i / s).
+void fill_rope_freq(RopeFreq& f, int d, double base, long double s = 1.0L);
 
 hipError_t launch_rope_apply(const void* x, void* y, const int32_t* pos, int B, int S, int H,
                              int d, int dt, const RopeFreq& f, hipStream_t stream);

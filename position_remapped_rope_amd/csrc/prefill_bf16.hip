@@ -9,7 +9,10 @@
 //            or with interpolated frequencies theta_i / s at p (same page,
 //            section 4.5): the remote pass reads ids floor(p / div) with the
 //            frequency table fr, div = s or 1
-// scaled by softmax_scale; causal, plus the window for NOPE/ROPE.
+// scaled by softmax_scale; causal, plus the window for NOPE/ROPE. Ids may be
+// negative: the period and the remote map use floor semantics. NOPE/ROPE may add
+// ALiBi biases - m_h (i - j) to the scaled scores (P-RoPE page, section 1: SWA
+// with ALiBi; the window clamps the penalty to the kept distances).
 //
 // Work decomposition. A workgroup (8 wavefronts, two per SIMD) owns 256 query
 // rows: HG query heads of one KV group times BMp = 256/HG consecutive
@@ -115,8 +118,8 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float c) {
 
 template <int MODE>
 __device__ __forceinline__ int rot_index(int p, int rot, const PrefillArgs& a) {
-  if (rot == 2) return static_cast<int>(fastdiv(static_cast<uint32_t>(p), a.scale_div));
-  if (MODE == kRope) return a.period > 0 ? static_cast<int>(fastmod(static_cast<uint32_t>(p), a.period_div)) : p;
+  if (rot == 2) return floordiv_s(p, a.scale_div);
+  if (MODE == kRope) return a.period > 0 ? floormod_s(p, a.period_div) : p;
   return p;
 }
 
@@ -135,7 +138,7 @@ __device__ __forceinline__ u32x4_t rotate_chunk(u32x4_t x, int r, const uint32_t
   return y;
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool ALIBI>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int KS = D / 16;                  // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;                  // 32-row blocks of O^T
@@ -281,8 +284,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   if (npass > 1) tile_range(dlo1, dhi1, tb1, tc1);
   const int T = tc0 + tc1;
 
+  // pass of tile t. Tiles past the last (t >= T, staged but never read) get a
+  // valid rotation kind too: NOPE/ROPE have pass 0 only, and bifocal's pass 1
+  // (base ids) is valid even without a local window.
+  auto pass_of = [&](int t) __attribute__((always_inline)) { return (MODE == kBifocal && t >= tc0) ? 1 : 0; };
   auto tile_of = [&](int t, int& p, int& kt) {
-    p = t < tc0 ? 0 : 1;
+    p = pass_of(t);
     kt = p ? tb1 + (t - tc0) : tb0 + t;
   };
 
@@ -508,6 +515,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   float m_run = -INFINITY;  // running max of scaled scores, log2 units
   float l_run = 0.f;        // this lane's share of the running sum
   const float sl2 = a.scale_log2;
+  // ALiBi slope of this wave's head in log2 units (the scores are kept in log2 units)
+  const float slope2 = ALIBI ? a.alibi[h] * 1.4426950408889634f : 0.f;
 
   // does tile t hold any kept (row, key) pair of this wave?
   auto wave_live = [&](int t, bool& need_mask, int& dlo, int& dhi, int& j0) __attribute__((always_inline)) {
@@ -525,7 +534,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     int dlo, dhi, j0;
     return wave_live(t, nm, dlo, dhi, j0);
   };
-  auto pass_of = [&](int t) __attribute__((always_inline)) { return t < tc0 ? 0 : 1; };
 
   auto xhalf_max = [&](float x) __attribute__((always_inline)) {
     // max with the lane 32 apart (same query row, other half of the keys)
@@ -578,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float sn, cs, y0, y1;
-      phase_sincos(phase_top_u(static_cast<uint32_t>(r0), kf_reg[e].x, kf_reg[e].y), sn, cs);
+      phase_sincos(phase_top(r0, kf_reg[e].x, kf_reg[e].y), sn, cs);
       rot_pair(bf16_lo(kraw[0][e]), bf16_hi(kraw[0][e]), cs, sn, y0, y1);
       krot[0][e] = pack_bf16(y0, y1);
       if (NU > 1) {  // the second row: one id step further, (cs + i sn) * (step cos + i step sin)
@@ -684,8 +692,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       rotate_k(t);
       return false;
     }
+    const int dbase = (i0 + lr) - (j0 + 4 * lg);  // i - j of register 0 of block 0
+    if (ALIBI) {  // logits in log2 units: s * scale - slope * (i - j)
+      const float b0 = -slope2 * static_cast<float>(dbase);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float c = static_cast<float>(nb * 32 + 8 * (r >> 2) + (r & 3));
+          sacc[nb][r] = fmaf(sacc[nb][r], sl2, fmaf(slope2, c, b0));
+        }
+    }
     if (need_mask) {
-      const int dbase = (i0 + lr) - (j0 + 4 * lg);  // i - j of register 0 of block 0
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -700,7 +718,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       mx0 = fmaxf(mx0, fmaxf(sacc[0][r], sacc[0][r + 1]));
       mx1 = fmaxf(mx1, fmaxf(sacc[1][r], sacc[1][r + 1]));
     }
-    const float mx = xhalf_max(fmaxf(mx0, mx1)) * sl2;
+    // sl2 > 0, so scaling after the max is the max of the scaled scores
+    const float smul = ALIBI ? 1.f : sl2;  // ALiBi scores are scaled already
+    const float mx = xhalf_max(fmaxf(mx0, mx1)) * smul;
     rotate_k(t);
     // The reference max moves only when the tile's max exceeds it by more than
     // 8 (log2 units): P <= 2^8 stays exact in bf16 and fp32, and O and l are
@@ -716,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       const int nb = kk >> 1, r0 = (kk & 1) * 8;
       float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r0 + e], sl2, -mref));
+      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r0 + e], smul, -mref));
       const u32x4_t w = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
                          pack_bf16(pv[6], pv[7])};
       pop[kk] = w;
@@ -820,15 +840,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 
 int64_t n_items(const PrefillArgs& a) { return int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks; }
 
-template <int D, int MODE>
+template <int D, int MODE, bool ALIBI = false>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   // one workgroup per item, or with a queue one per compute unit (a workgroup
   // fills a CU: 8 waves at 2 per SIMD)
   const int64_t n = n_items(a);
   const int64_t grid = a.queue ? (n < a.n_cu ? n : a.n_cu) : n;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, MODE, ALIBI>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
+  if (a.alibi) return a.mode == kNope ? launch_t<D, kNope, true>(a, stream) : launch_t<D, kRope, true>(a, stream);
+  switch (a.mode) {
+    case kNope: return launch_t<D, kNope>(a, stream);
+    case kRope: return launch_t<D, kRope>(a, stream);
+    default: return launch_t<D, kBifocal>(a, stream);
+  }
 }
 
 }  // namespace
@@ -838,18 +868,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 bool prefill_bf16_fits(const PrefillArgs& a) { return n_items(a) * kThreads <= kMaxWorkItems; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-  if (a.D == 128) {
-    switch (a.mode) {
-      case kNope: return launch_t<128, kNope>(a, stream);
-      case kRope: return launch_t<128, kRope>(a, stream);
-      default: return launch_t<128, kBifocal>(a, stream);
-    }
-  }
-  switch (a.mode) {
-    case kNope: return launch_t<64, kNope>(a, stream);
-    case kRope: return launch_t<64, kRope>(a, stream);
-    default: return launch_t<64, kBifocal>(a, stream);
-  }
+  return a.D == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
 }
 
 }  // namespace prope

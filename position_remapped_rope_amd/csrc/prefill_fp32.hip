@@ -11,6 +11,8 @@
 // Jet-Long Eq. (7) with disjoint parts). With the keys split this way a
 // row's tiles run 8 at a time instead of one after another: a short problem
 // is bound by the latency of its longest rows' tile loop, at one wave per SIMD.
+// ALiBi slopes (NOPE/ROPE), when given, subtract m_h (i - j) from each scaled
+// score (P-RoPE page, section 1).
 #include <limits.h>
 
 #include "internal.hpp"
@@ -46,8 +48,8 @@ __device__ __forceinline__ float row_group_sum(float x) {
 
 template <int MODE>
 __device__ __forceinline__ int rot_index_f(int p, int rot, const PrefillArgs& a) {
-  if (rot == 2) return static_cast<int>(fastdiv(static_cast<uint32_t>(p), a.scale_div));
-  if (MODE == kRope) return a.period > 0 ? static_cast<int>(fastmod(static_cast<uint32_t>(p), a.period_div)) : p;
+  if (rot == 2) return floordiv_s(p, a.scale_div);
+  if (MODE == kRope) return a.period > 0 ? floormod_s(p, a.period_div) : p;
   return p;
 }
 
@@ -110,6 +112,8 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
   for (int c = 0; c < DH; ++c) o[c] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale_log2;
+  // ALiBi slope of this row's head, log2 units (0 without ALiBi: the bias term vanishes)
+  const float slope2 = (MODE != kBifocal && a.alibi) ? a.alibi[h] * 1.4426950408889634f : 0.f;
 
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(kThreadsF) void prefill_fp32_kernel(const PrefillAr
         acc = row_group_sum<TPR>(acc);
         const int dist = i - (j0 + n);
         const bool keep = dist >= dlo[p] && dist <= dhi[p] && j0 + n < S;
-        sc[n] = keep ? acc * sl2 : -INFINITY;
+        sc[n] = keep ? fmaf(acc, sl2, -slope2 * static_cast<float>(dist)) : -INFINITY;
         mx = fmaxf(mx, sc[n]);
       }
       const float mnew = fmaxf(m_run, mx);

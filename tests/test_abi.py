@@ -39,7 +39,7 @@ def test_header_symbols_exported():
 
 def test_status_strings_and_version():
     L = P.lib()
-    assert L.prope_version() == 1
+    assert L.prope_version() == 2
     for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, 12345):
         assert isinstance(P.status_string(code), str) and P.status_string(code)
 
@@ -53,10 +53,32 @@ def test_group_size_golden():
 
 def _params(**kw):
     d = dict(mode=P.BIFOCAL, period=0, remap_scale=2, window_left=8, rope_base=1e6, softmax_scale=0.0, w_pretrained=0,
-             remote_map=0)
+             remote_map=0, reserved=0, interp_scale=0.0, alibi_slopes=None)
     d.update(kw)
     return P.PropeParams(d["mode"], d["period"], d["remap_scale"], d["window_left"], d["rope_base"],
-                         d["softmax_scale"], d["w_pretrained"], d["remote_map"])
+                         d["softmax_scale"], d["w_pretrained"], d["remote_map"], d["reserved"], d["interp_scale"],
+                         d["alibi_slopes"])
+
+
+def test_params_layout_matches_header(tmp_path):
+    """The binding's ctypes struct has the C struct's size and field offsets."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in P.PropeParams._fields_]
+    body = "".join(f'  printf("{f} %zu\\n", offsetof(prope_params, {f}));\n' for f in fields)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "prope.h"\nint main(void) {\n'
+                   '  printf("sizeof %zu\\n", sizeof(prope_params));\n' + body + '  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    r = subprocess.run([cc, "-std=c99", f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    assert int(got["sizeof"]) == ctypes.sizeof(P.PropeParams)
+    for f in fields:
+        assert int(got[f]) == getattr(P.PropeParams, f).offset, f
 
 
 def _prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos=FAKE, B=1, S=16, Hq=4, Hkv=2, d=128, dt=0,
@@ -82,6 +104,14 @@ def _prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, pos=FAKE, B=1, S=16, Hq=4
     dict(params=_params(mode=P.ROPE, remap_scale=1, w_pretrained=64)),  # dynamic G is bifocal only
     dict(params=_params(remote_map=2)), dict(params=_params(remote_map=-1)),
     dict(params=_params(mode=P.ROPE, remap_scale=1, remote_map=1)),     # interpolation is bifocal only
+    dict(params=_params(reserved=1)),
+    dict(params=_params(remap_scale=1, remote_map=1, interp_scale=0.5)),           # s >= 1
+    dict(params=_params(remap_scale=1, remote_map=1, interp_scale=float("nan"))),
+    dict(params=_params(remap_scale=1, remote_map=1, interp_scale=float("inf"))),
+    dict(params=_params(remap_scale=1, remote_map=0, interp_scale=1.5)),           # real s is interpolation only
+    dict(params=_params(remap_scale=2, remote_map=1, interp_scale=1.5)),           # one source of s
+    dict(params=_params(remap_scale=1, remote_map=1, interp_scale=1.5, w_pretrained=64)),
+    dict(params=_params(alibi_slopes=FAKE)),                                        # ALiBi is nope/rope only
     dict(byref=False),
 ])
 def test_prefill_rejects(kw):
@@ -123,7 +153,8 @@ def _decode(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, kv_len=FAKE, B=1, Lmax=4096, Hq=32
     (dict(Lmax=1 << 21, Hkv=8, Hq=32), UNSUPPORTED),
     (dict(B=65536, Lmax=1024), UNSUPPORTED), (dict(Hq=65536, Hkv=65536, Lmax=16, d=64), UNSUPPORTED),
     (dict(ws_bytes=100), WORKSPACE),
-    (dict(params=_params(remap_scale=1, w_pretrained=4096, remote_map=1)), UNSUPPORTED),
+    (dict(params=_params(alibi_slopes=FAKE)), INVALID),
+    (dict(params=_params(remap_scale=1, remote_map=1, interp_scale=0.99)), INVALID),
 ])
 def test_decode_rejects(kw, code):
     assert _decode(**kw) == code
@@ -143,7 +174,7 @@ def _unfused(q=FAKE, k=FAKE, v=FAKE, o=FAKE, pos=FAKE, B=1, S=1000, Hq=4, Hkv=2,
     (dict(params=_params(mode=P.ROPE, remap_scale=1)), INVALID), (dict(params=_params(mode=P.NOPE, remap_scale=1)), INVALID),
     (dict(pos=None), INVALID), (dict(ws=None), INVALID), (dict(ws=FAKE + 16), INVALID),
     (dict(ws_bytes=1000), WORKSPACE), (dict(d=96), INVALID), (dict(Hq=5, Hkv=2), INVALID),
-    (dict(params=_params(remote_map=1)), UNSUPPORTED),
+    (dict(params=_params(remap_scale=1, remote_map=1, interp_scale=0.5)), INVALID),
 ])
 def test_unfused_rejects(kw, code):
     assert _unfused(**kw) == code
@@ -206,3 +237,69 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(P, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(P.PropeError):
         P.lib()
+
+
+# ---------------------------------------------------------------- binding argument checks
+# The C ABI cannot see buffer sizes, so the binding checks every caller-supplied
+# output and the operand dtypes before it calls into the library. Device checks
+# are switched off here (no GPU), so CPU tensors reach the shape checks; every
+# case raises before a library call.
+
+@pytest.fixture
+def cpu_binding(monkeypatch):
+    monkeypatch.setattr(P, "_dev", lambda t, name: None)
+    return P
+
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["out_shape", "out_dtype", "lse_shape", "lse_dtype", "slopes_shape", "slopes_dtype"])
+def test_binding_prefill_rejects_mismatched_outputs(cpu_binding, case):
+    import torch
+    q, k, v = _t(1, 16, 4, 64), _t(1, 16, 2, 64), _t(1, 16, 2, 64)
+    pos = torch.zeros((1, 16), dtype=torch.int32)
+    kw = {
+        "out_shape": dict(out=_t(1, 15, 4, 64)),
+        "out_dtype": dict(out=_t(1, 16, 4, 64, dtype=torch.float32)),
+        "lse_shape": dict(lse=_t(1, 16, 4, dtype=torch.float32)),
+        "lse_dtype": dict(lse=_t(1, 4, 16)),
+        "slopes_shape": dict(alibi_slopes=_t(3, dtype=torch.float32)),
+        "slopes_dtype": dict(alibi_slopes=_t(4)),
+    }[case]
+    with pytest.raises(P.PropeError):
+        P.prefill(q, k, v, pos, mode="rope", **kw)
+
+
+@pytest.mark.parametrize("case", ["out_shape", "lse_shape", "q_dtype", "cache_dtype", "slopes"])
+def test_binding_decode_rejects_mismatched_operands(cpu_binding, case):
+    import torch
+    q, kc, vc = _t(2, 8, 64), _t(2, 100, 2, 64), _t(2, 100, 2, 64)
+    kv_len = torch.zeros((2,), dtype=torch.int32)
+    kw = {}
+    if case == "out_shape":
+        kw = dict(out=_t(2, 8, 32))
+    elif case == "lse_shape":
+        kw = dict(lse=_t(2, 4, dtype=torch.float32))
+    elif case == "q_dtype":
+        q = _t(2, 8, 64, dtype=torch.float32)
+    elif case == "cache_dtype":
+        vc = _t(2, 100, 2, 64, dtype=torch.float32)
+    else:
+        kw = dict(mode="nope", alibi_slopes=_t(2, dtype=torch.float32))
+    with pytest.raises(P.PropeError):
+        P.decode(q, kc, vc, kv_len, **kw)
+
+
+def test_binding_rope_apply_and_unfused_reject_mismatched_outputs(cpu_binding):
+    import torch
+    x = _t(1, 8, 2, 64)
+    pos = torch.zeros((1, 8), dtype=torch.int32)
+    with pytest.raises(P.PropeError):
+        P.rope_apply(x, pos, 1e4, out=_t(1, 8, 2, 32))
+    q, k, v = _t(1, 16, 4, 64), _t(1, 16, 2, 64), _t(1, 16, 2, 64)
+    with pytest.raises(P.PropeError):
+        P.prefill_bifocal_unfused(q, k, v, torch.zeros((1, 16), dtype=torch.int32), remap_scale=2, window_left=3,
+                                  lse=_t(1, 4, 15, dtype=torch.float32))
