@@ -265,13 +265,14 @@ def test_two_graphs_on_one_capture_stream_replay_in_any_order():
     """Two prefill graphs captured on the same side stream (each capture gets its
     own zero-filled queue buffer) replay in either order, and back to back, to the
     eager results."""
-    outs, refs, graphs = [], [], []
+    outs, refs, graphs, keep = [], [], [], []
     side = torch.cuda.Stream(device=DEV)
     for i, (mode, kw) in enumerate([("bifocal", dict(rope_base=1e6, remap_scale=2, window_left=300)),
                                     ("rope", dict(rope_base=1e4, period=256, window_left=127))]):
         inp = _inputs(1, 2500, 8, 2, 128, "bf16", seed=530 + i)
         q, k, v, pos = (inp[n].to(DEV) for n in ("q", "k", "v", "pos"))
         o = torch.empty_like(q)
+        keep.append((q, k, v, pos))  # a graph does not keep its inputs alive
         run = (lambda q=q, k=k, v=v, pos=pos, o=o, mode=mode, kw=kw:
                P.prefill(q, k, v, pos, mode=mode, out=o, **kw))
         run()
