@@ -214,6 +214,29 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
                       void* stream);
 
 /*
+ * Decode as prope_attn_decode (same arguments, checks and results, bit for bit)
+ * for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The split-K partials go
+ * to a fixed device array inside the library instead of a caller workspace:
+ * PROPE_DECODE_SCRATCH_BYTES per device, held from when the library's code is
+ * loaded on the device until the process ends. The array's device address is
+ * looked up on the first call on each device (a HIP call, no allocation).
+ *   A call fits when its partials, B * Hq * chunks * (d + 2) * 4 bytes for the
+ *   launch's chunk choice, fit the array; any call with
+ *   prope_decode_workspace_size(B, Lmax, Hq, d) <= PROPE_DECODE_SCRATCH_BYTES
+ *   does (the 128K-key batch-8 decode with 32 query heads needs 8.5 MB).
+ *   Otherwise PROPE_ERR_WORKSPACE, before any HIP call.
+ *   Every call on a device shares its one array, which keeps the last call's
+ *   contents (none of it needs to start at zero): calls that may overlap on
+ *   one device (other streams, concurrent graph replays) race and must be
+ *   ordered by the caller.
+ */
+#define PROPE_DECODE_SCRATCH_BYTES (16u << 20)
+int prope_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                              const int32_t* kv_len, int B, int Lmax, int Hq, int Hkv, int d, int dt,
+                              const prope_params* params, void* stream);
+
+/*
  * y = R_pos x per token and head (P-RoPE page, Eq. (2)): x, y [B,S,H,d] of
  * dtype `dt`, pos [B,S] int32 (any sign: a negative id rotates backwards, which
  * applies Jet-Long's Eq. (6) corrections). y may alias x exactly. d even,

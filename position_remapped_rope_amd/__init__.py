@@ -12,7 +12,8 @@ import os
 from typing import Optional
 
 __all__ = ["NOPE", "ROPE", "BIFOCAL", "PropeError", "lib", "lib_path", "rope_apply", "prefill", "prefill_queue",
-           "prefill_bifocal_unfused", "bifocal_unfused_workspace_size", "decode", "decode_workspace_size",
+           "prefill_bifocal_unfused", "bifocal_unfused_workspace_size", "decode", "decode_noalloc",
+           "decode_workspace_size", "DECODE_SCRATCH_BYTES",
            "group_size", "status_string", "EXPORTED_SYMBOLS"]
 
 NOPE, ROPE, BIFOCAL = 0, 1, 2
@@ -20,10 +21,12 @@ _MODES = {"nope": NOPE, "rope": ROPE, "bifocal": BIFOCAL}
 REMOTE_ALIAS, REMOTE_INTERP = 0, 1
 _REMOTE = {"alias": REMOTE_ALIAS, "interp": REMOTE_INTERP}
 BF16, FP32 = 0, 1
+DECODE_SCRATCH_BYTES = 16 << 20  # PROPE_DECODE_SCRATCH_BYTES
 
 EXPORTED_SYMBOLS = ("prope_attn_prefill", "prope_attn_prefill_queued", "prope_prefill_queue_size",
                     "prope_attn_prefill_bifocal_unfused",
-                    "prope_bifocal_unfused_workspace_size", "prope_attn_decode", "prope_decode_workspace_size",
+                    "prope_bifocal_unfused_workspace_size", "prope_attn_decode", "prope_attn_decode_noalloc",
+                    "prope_decode_workspace_size",
                     "prope_rope_apply", "prope_group_size", "prope_status_string", "prope_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +78,9 @@ def lib():
     L.prope_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                     ctypes.POINTER(PropeParams), vp, ctypes.c_size_t, vp]
     L.prope_attn_decode.restype = i32
+    L.prope_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(PropeParams), vp]
+    L.prope_attn_decode_noalloc.restype = i32
     L.prope_decode_workspace_size.argtypes = [i32, i32, i32, i32]
     L.prope_decode_workspace_size.restype = ctypes.c_size_t
     L.prope_rope_apply.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_double, vp]
@@ -292,7 +298,7 @@ def prefill_bifocal_unfused(q, k, v, pos, rope_base: float = 1e6, remap_scale: i
 def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
            remap_scale: int = 1, window_left: int = -1, softmax_scale: float = 0.0,
            out=None, lse=None, workspace=None, return_lse: bool = False, w_pretrained: int = 0,
-           remote_map="alias", interp_scale: float = 0.0, alibi_slopes=None):
+           remote_map="alias", interp_scale: float = 0.0, alibi_slopes=None, _noalloc: bool = False):
     """One decode step: q [B,Hq,d] base-rotated, caches [B,Lmax,Hkv,d], kv_len int32 [B]."""
     import torch
     L = lib()
@@ -315,14 +321,25 @@ def decode(q, k_cache, v_cache, kv_len, mode="bifocal", rope_base: float = 1e6,
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    need = L.prope_decode_workspace_size(B, Lmax, Hq, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     slopes = _slopes(alibi_slopes, Hq, q.device)
     p = _params(mode, rope_base, 0, remap_scale, window_left, softmax_scale, w_pretrained, remote_map,
                 interp_scale, slopes)
-    _check(L.prope_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
-                               _ptr(kv_len), B, Lmax, Hq, Hkv, d, _dtype_code(q), ctypes.byref(p),
-                               _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               _stream(q)))
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(kv_len), B, Lmax, Hq, Hkv, d,
+            _dtype_code(q), ctypes.byref(p))
+    if _noalloc:
+        if workspace is not None:
+            raise PropeError("the no-allocation decode takes no workspace")
+        _check(L.prope_attn_decode_noalloc(*args, _stream(q)))
+        return (o, lse) if return_lse else o
+    need = L.prope_decode_workspace_size(B, Lmax, Hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(L.prope_attn_decode(*args, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, lse) if return_lse else o
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_len, out=None, lse=None, return_lse: bool = False, **kw):
+    """decode() through prope_attn_decode_noalloc: the split-K partials live in the
+    library's fixed device array (DECODE_SCRATCH_BYTES per device), so the call
+    allocates no device memory when `out` (and `lse`, if wanted) are given."""
+    return decode(q, k_cache, v_cache, kv_len, out=out, lse=lse, return_lse=return_lse, _noalloc=True, **kw)

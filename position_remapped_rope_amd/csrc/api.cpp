@@ -209,6 +209,71 @@ UnfusedLayout unfused_layout(int B, int S, int Hq, int d, int dt) {
   return l;
 }
 
+// Validation and launch set-up shared by the decode entry points (everything
+// but the workspace). The chunk policy is described above kDecodeChunkRows.
+int decode_setup(DecodeArgs& a, const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                 const int32_t* kv_len, int B, int Lmax, int Hq, int Hkv, int d, int dt,
+                 const prope_params* params) {
+  const int pc = check_params(params, true);
+  if (pc != PROPE_OK) return pc;
+  if (!q || !k_cache || !v_cache || !o || !kv_len) return PROPE_ERR_INVALID_ARG;
+  if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || (Hq % Hkv)) return PROPE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return PROPE_ERR_INVALID_ARG;
+  if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
+  if (dt != PROPE_BF16) return PROPE_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return PROPE_ERR_UNSUPPORTED;  // query heads of a group fill one 16-wide MFMA tile
+  if (B > 65535 || Hkv > 65535) return PROPE_ERR_UNSUPPORTED;  // grid y and z limits
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(o)) % 16)
+    return PROPE_ERR_INVALID_ARG;
+  // one sequence's cache slice is addressed with 32-bit byte offsets
+  if (int64_t(Lmax) * Hkv * d * 2 >= (int64_t(1) << 32)) return PROPE_ERR_UNSUPPORTED;
+  const bool interp = params->remote_map == PROPE_REMOTE_INTERP;
+
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_len = kv_len;
+  a.ws = nullptr;
+  a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv; a.D = d; a.G = Hq / Hkv;
+  const int n_cu = device_cus();
+  const int64_t wg_rows = int64_t(B) * (Hkv / 4) * ((Lmax + kDecodeChunkRows - 1) / kDecodeChunkRows);
+  const int64_t wg_large = int64_t(B) * Hkv * ((Lmax + kDecodeChunkLarge - 1) / kDecodeChunkLarge);
+  if (Hkv % 4 == 0 && wg_rows <= n_cu) {
+    a.hpw = 4;
+    a.chunk = kDecodeChunkRows;
+  } else {
+    a.hpw = 1;
+    a.chunk = wg_large <= n_cu ? kDecodeChunkLarge : kDecodeChunk;
+  }
+  // Short caches: halve the chunk while the grid has fewer than kDecodeMinGrid
+  // workgroups, down to kDecodeMinWaveKeys keys per wave, so that the waves'
+  // serial key loops get shorter instead of most of the chip idling.
+  const int kw = 4 / a.hpw;
+  auto grid = [&](int c) { return int64_t(B) * (Hkv / a.hpw) * ((Lmax + c - 1) / c); };
+  while (grid(a.chunk) < kDecodeMinGrid && a.chunk / 2 >= kDecodeMinWaveKeys * kw) a.chunk /= 2;
+  a.n_chunks = (Lmax + a.chunk - 1) / a.chunk;
+  a.mode = params->mode;
+  a.window_left = params->window_left;
+  a.scale_div = make_fastdiv(static_cast<uint32_t>(interp ? 1 : params->remap_scale));
+  a.w_pre = params->w_pretrained;
+  a.scale_log2 = scale_log2(params, d);
+  a.alibi = params->alibi_slopes;
+  fill_rope_freq(a.f, d, params->mode == PROPE_NOPE ? 10000.0 : params->rope_base);
+  a.interp = interp;
+  if (interp && a.w_pre > 0) {
+    a.fr = a.f;  // per sequence: the kernel forms theta_i / s - theta_i from f and kv_len
+  } else if (interp) {  // correction frequencies theta_i / s - theta_i, modulo one turn
+    RopeFreq fs;
+    fill_rope_freq(fs, d, params->rope_base, interp_scale(*params, Lmax));
+    for (int i = 0; i < kMaxPairs; ++i) {
+      const uint64_t c = ((uint64_t(fs.hi[i]) << 32) | fs.lo[i]) - ((uint64_t(a.f.hi[i]) << 32) | a.f.lo[i]);
+      a.fr.lo[i] = static_cast<uint32_t>(c);
+      a.fr.hi[i] = static_cast<uint32_t>(c >> 32);
+    }
+  } else {
+    a.fr = a.f;
+  }
+  return PROPE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -353,66 +418,28 @@ int prope_attn_decode(const void* q, const void* k_cache, const void* v_cache, v
                       const int32_t* kv_len, int B, int Lmax, int Hq, int Hkv, int d, int dt,
                       const prope_params* params, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  const int pc = check_params(params, true);
-  if (pc != PROPE_OK) return pc;
-  if (!q || !k_cache || !v_cache || !o || !kv_len || !workspace) return PROPE_ERR_INVALID_ARG;
-  if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || (Hq % Hkv)) return PROPE_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return PROPE_ERR_INVALID_ARG;
-  if (dt != PROPE_BF16 && dt != PROPE_FP32) return PROPE_ERR_INVALID_ARG;
-  if (dt != PROPE_BF16) return PROPE_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 16) return PROPE_ERR_UNSUPPORTED;  // query heads of a group fill one 16-wide MFMA tile
-  if (B > 65535 || Hkv > 65535) return PROPE_ERR_UNSUPPORTED;  // grid y and z limits
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
-       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(o) |
-       reinterpret_cast<uintptr_t>(workspace)) % 16)
-    return PROPE_ERR_INVALID_ARG;
-  const bool interp = params->remote_map == PROPE_REMOTE_INTERP;
-  if (workspace_bytes < prope_decode_workspace_size(B, Lmax, Hq, d)) return PROPE_ERR_WORKSPACE;
-  // one sequence's cache slice is addressed with 32-bit byte offsets
-  if (int64_t(Lmax) * Hkv * d * 2 >= (int64_t(1) << 32)) return PROPE_ERR_UNSUPPORTED;
-
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 16) return PROPE_ERR_INVALID_ARG;
   DecodeArgs a{};
-  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_len = kv_len;
+  const int rc = decode_setup(a, q, k_cache, v_cache, o, lse, kv_len, B, Lmax, Hq, Hkv, d, dt, params);
+  if (rc != PROPE_OK) return rc;
+  if (workspace_bytes < prope_decode_workspace_size(B, Lmax, Hq, d)) return PROPE_ERR_WORKSPACE;
   a.ws = static_cast<float*>(workspace);
-  a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv; a.D = d; a.G = Hq / Hkv;
-  const int n_cu = device_cus();
-  const int64_t wg_rows = int64_t(B) * (Hkv / 4) * ((Lmax + kDecodeChunkRows - 1) / kDecodeChunkRows);
-  const int64_t wg_large = int64_t(B) * Hkv * ((Lmax + kDecodeChunkLarge - 1) / kDecodeChunkLarge);
-  if (Hkv % 4 == 0 && wg_rows <= n_cu) {
-    a.hpw = 4;
-    a.chunk = kDecodeChunkRows;
-  } else {
-    a.hpw = 1;
-    a.chunk = wg_large <= n_cu ? kDecodeChunkLarge : kDecodeChunk;
-  }
-  // Short caches: halve the chunk while the grid has fewer than kDecodeMinGrid
-  // workgroups, down to kDecodeMinWaveKeys keys per wave, so that the waves'
-  // serial key loops get shorter instead of most of the chip idling.
-  const int kw = 4 / a.hpw;
-  auto grid = [&](int c) { return int64_t(B) * (Hkv / a.hpw) * ((Lmax + c - 1) / c); };
-  while (grid(a.chunk) < kDecodeMinGrid && a.chunk / 2 >= kDecodeMinWaveKeys * kw) a.chunk /= 2;
-  a.n_chunks = (Lmax + a.chunk - 1) / a.chunk;
-  a.mode = params->mode;
-  a.window_left = params->window_left;
-  a.scale_div = make_fastdiv(static_cast<uint32_t>(interp ? 1 : params->remap_scale));
-  a.w_pre = params->w_pretrained;
-  a.scale_log2 = scale_log2(params, d);
-  a.alibi = params->alibi_slopes;
-  fill_rope_freq(a.f, d, params->mode == PROPE_NOPE ? 10000.0 : params->rope_base);
-  a.interp = interp;
-  if (interp && a.w_pre > 0) {
-    a.fr = a.f;  // per sequence: the kernel forms theta_i / s - theta_i from f and kv_len
-  } else if (interp) {  // correction frequencies theta_i / s - theta_i, modulo one turn
-    RopeFreq fs;
-    fill_rope_freq(fs, d, params->rope_base, interp_scale(*params, Lmax));
-    for (int i = 0; i < kMaxPairs; ++i) {
-      const uint64_t c = ((uint64_t(fs.hi[i]) << 32) | fs.lo[i]) - ((uint64_t(a.f.hi[i]) << 32) | a.f.lo[i]);
-      a.fr.lo[i] = static_cast<uint32_t>(c);
-      a.fr.hi[i] = static_cast<uint32_t>(c >> 32);
-    }
-  } else {
-    a.fr = a.f;
-  }
+  const hipError_t e = launch_decode_bf16(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PROPE_OK : PROPE_ERR_HIP;
+}
+
+int prope_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                              const int32_t* kv_len, int B, int Lmax, int Hq, int Hkv, int d, int dt,
+                              const prope_params* params, void* stream) {
+  DecodeArgs a{};
+  const int rc = decode_setup(a, q, k_cache, v_cache, o, lse, kv_len, B, Lmax, Hq, Hkv, d, dt, params);
+  if (rc != PROPE_OK) return rc;
+  // the partials of this launch's chunk choice must fit the fixed array
+  if (size_t(B) * Hq * a.n_chunks * (size_t(d) + 2) * sizeof(float) > kDecodeScratchBytes)
+    return PROPE_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (decode_scratch(&scratch) != hipSuccess) return PROPE_ERR_HIP;
+  a.ws = static_cast<float*>(scratch);
   const hipError_t e = launch_decode_bf16(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PROPE_OK : PROPE_ERR_HIP;
 }

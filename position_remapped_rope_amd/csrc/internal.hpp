@@ -86,6 +86,10 @@ constexpr int64_t kMaxWorkItems = 0xffffffffLL;
 bool prefill_bf16_fits(const PrefillArgs& a);
 bool prefill_fp32_fits(const PrefillArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// The fixed device array that prope_attn_decode_noalloc uses for its split-K
+// partials (decode_scratch.hip): its size, and its address on the current device.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_remap_ids(const int32_t* pos, int32_t* out, int64_t n, const FastDiv& s, hipStream_t stream);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream);
 hipError_t launch_eq7_merge(const void* oa, const float* la, void* o, const float* lb, const void* oc,

@@ -303,3 +303,20 @@ def test_binding_rope_apply_and_unfused_reject_mismatched_outputs(cpu_binding):
     with pytest.raises(P.PropeError):
         P.prefill_bifocal_unfused(q, k, v, torch.zeros((1, 16), dtype=torch.int32), remap_scale=2, window_left=3,
                                   lse=_t(1, 4, 15, dtype=torch.float32))
+
+
+def _decode_noalloc(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, kv_len=FAKE, B=1, Lmax=4096, Hq=32, Hkv=8, d=128, dt=0,
+                    params=None):
+    L = P.lib()
+    p = _params() if params is None else params
+    return L.prope_attn_decode_noalloc(q, kc, vc, o, None, kv_len, B, Lmax, Hq, Hkv, d, dt, ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(kv_len=None), INVALID), (dict(o=FAKE + 8), INVALID), (dict(d=80), INVALID),
+    (dict(dt=1), UNSUPPORTED),
+    # partials beyond the fixed 16 MiB array: 64 x 32 heads x 64 chunks x 130 x 4 B
+    (dict(B=64, Lmax=131072), WORKSPACE),
+])
+def test_decode_noalloc_rejects(kw, code):
+    assert _decode_noalloc(**kw) == code

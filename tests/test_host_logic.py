@@ -42,7 +42,7 @@ def test_no_kernel_spills_to_scratch(tmp_path):
         assert r.returncode == 0, r.stderr
         names = re.findall(r"Function Name: (\S+)", r.stderr)
         scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", r.stderr)]
-        assert len(names) == len(scratch) and names, src
+        assert len(names) == len(scratch), src  # (a source may hold no kernel)
         for n, sc in zip(names, scratch):
             assert sc == 0, f"{src}: {n} uses {sc} bytes of scratch per lane"
         seen += len(names)
