@@ -33,7 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libprope.so")
+    """The in-tree libprope.so, or the build PROPE_LIB_PATH names (e.g. a host-sanitized copy)."""
+    return os.environ.get("PROPE_LIB_PATH") or os.path.join(_HERE, "libprope.so")
 
 
 class PropeError(RuntimeError):

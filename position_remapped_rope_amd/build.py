@@ -1,6 +1,11 @@
 """Build libprope.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m position_remapped_rope_amd.build [-v]
+Usage: python -m position_remapped_rope_amd.build [-v] [--sanitize OUT.so]
+
+--sanitize builds a copy whose host code (argument checks, launch set-up,
+integer helpers) carries AddressSanitizer and UndefinedBehaviorSanitizer; the
+device code is built as usual. Load it with the ASan runtime preloaded
+(libclang_rt.asan-x86_64.so), for CPU-side tests.
 """
 from __future__ import annotations
 
@@ -36,12 +41,26 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+# host-only sanitizers: every -fsanitize= is bound to the host pass
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime that a process loading a sanitized build must preload."""
+    import glob
+    cands = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not cands:
+        raise RuntimeError("clang ASan runtime not found")
+    return cands[-1]
+
+
+def _compile(src: str, verbose: bool, build_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     # device sources: no kernel relies on NaN semantics, so max() needs no
     # canonicalisation; host argument checks (api.cpp) keep IEEE NaN handling
     lang = ["-x", "hip", "-fno-honor-nans"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,21 +71,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link libprope.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize_out: str = "") -> str:
+    """Compile every source (in parallel) and link libprope.so; returns its path.
+    With sanitize_out, link a host-sanitized copy there instead."""
+    build_dir = os.path.join(BUILD_DIR, "asan") if sanitize_out else BUILD_DIR
+    extra = SANITIZE_FLAGS if sanitize_out else []
+    out = sanitize_out or OUT
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = OUT + ".tmp"
-    cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *extra, "-shared-libsan", "-o", tmp, *objs] \
+        if sanitize_out else [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    san = sys.argv[sys.argv.index("--sanitize") + 1] if "--sanitize" in sys.argv else ""
+    print(build(verbose="-v" in sys.argv, sanitize_out=san))

@@ -72,7 +72,7 @@ int check_params(const prope_params* p, bool decode) {
 // group size of Jet-Long Eq. (2) when w_pretrained > 0.
 int remote_scale(const prope_params& p, int64_t L) {
   if (p.w_pretrained <= 0) return p.remap_scale;
-  const int64_t g = (L + p.w_pretrained - 1) / p.w_pretrained;
+  const int64_t g = L / p.w_pretrained + (L % p.w_pretrained != 0);
   return g < 1 ? 1 : static_cast<int>(g);
 }
 
@@ -294,7 +294,7 @@ const char* prope_status_string(int status) {
 int prope_group_size(int64_t L, int64_t w_pretrained) {
   // Jet-Long section 3.1, Eq. (2).
   if (L < 0 || w_pretrained < 1) return -1;
-  const int64_t g = (L + w_pretrained - 1) / w_pretrained;
+  const int64_t g = L / w_pretrained + (L % w_pretrained != 0);  // ceil without overflow at L near 2^63
   if (g > INT32_MAX) return -1;
   return g < 1 ? 1 : static_cast<int>(g);
 }

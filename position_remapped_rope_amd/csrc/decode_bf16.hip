@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(kvh) * G) * D;
   u32x4_t qloc[KSTEPS], qrem[KSTEPS];
   // remote scale: fixed, or Jet-Long Eq. (2)'s group size for this sequence's length
-  const FastDiv sdv = a.w_pre > 0 ? make_fastdiv(static_cast<uint32_t>(max(1, (L + a.w_pre - 1) / a.w_pre)))
+  const FastDiv sdv = a.w_pre > 0 ? make_fastdiv(static_cast<uint32_t>(max(1, L / a.w_pre + (L % a.w_pre != 0))))
                                   : a.scale_div;
   // correction index of position x: floor(x/s) - x (alias) or x itself (interpolation,
   // whose correction frequencies theta_i / s - theta_i are in fr)

@@ -49,6 +49,10 @@ def test_group_size_golden():
     for L_, G in g["cases"]:
         assert P.group_size(L_, g["w_pretrained"]) == G
     assert P.group_size(10, 0) == -1 and P.group_size(-1, 5) == -1
+    # ceil(L / w) near the top of int64 (no overflow), and results beyond int32
+    assert P.group_size(2 ** 63 - 1, 2) == -1
+    assert P.group_size(2 ** 63 - 1, 2 ** 62) == 2
+    assert P.group_size(2 ** 31 - 1, 1) == 2 ** 31 - 1
 
 
 def _params(**kw):
