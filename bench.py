@@ -310,7 +310,7 @@ def main():
         return
 
     w, inp, pre = bench_prefill("bifocal_64k", args.steps, args.warmup)
-    sha = kernel_source_sha(["prefill_bf16.hip", "common.hpp", "internal.hpp"])
+    sha = kernel_source_sha(["prefill_bf16.hip", "prefill_common.hpp", "common.hpp", "internal.hpp"])
     traffic = load_traffic("prefill_bf16_bifocal_64k", sha)
     result = {
         "metric": METRIC,
