@@ -81,7 +81,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int lr = lane & 31, lg = lane >> 5;
   const int group = wave >> 2;  // waves w and w + 4 share a SIMD
 
+  // Per-chunk constants kept in LDS rather than registers: the 4 pair
+  // frequencies of each 16-byte column chunk, and for each rotation kind the
+  // cos/sin of the affine id step between the two K rows a thread stages. The
+  // second K row a thread stages is RPS keys after the first; when their
+  // rotation ids differ by that step (RPS for base ids, RPS / s for remote ids
+  // when s divides RPS) its cos/sin are the first row's times the step's.
+  __shared__ uint2 kfreq[2][CPR * 4];  // [0]: base frequencies, [1]: remote frequencies
+  __shared__ float2 kstep[2][CPR * 4];
+  const int id_step1 = NU > 1 ? RPS : -1;
+  const int sdiv = static_cast<int>(a.scale_div.div);
+  const int id_step2 = (NU > 1 && RPS % sdiv == 0) ? RPS / sdiv : -1;
+  if (MODE != kNope && tid < CPR * 4) {
+    const uint32_t flo = a.f.lo[tid], fhi = a.f.hi[tid];
+    const uint32_t rlo = a.fr.lo[tid], rhi = a.fr.hi[tid];
+    kfreq[0][tid] = make_uint2(flo, fhi);
+    kfreq[1][tid] = make_uint2(rlo, rhi);
+    float s1 = 0.f, c1 = 1.f, s2 = 0.f, c2 = 1.f;
+    if (id_step1 >= 0) rope_sincos(id_step1, flo, fhi, s1, c1);
+    if (id_step2 >= 0) rope_sincos(id_step2, rlo, rhi, s2, c2);
+    kstep[0][tid] = make_float2(c1, s1);
+    kstep[1][tid] = make_float2(c2, s2);
+  }
   // ---- work items (one per workgroup, or from the per-XCD queues) --------------
+  // (the barrier after each claim also publishes the tables above)
   ItemQueue iq(a);
   __shared__ int s_item;
 #pragma clang loop unroll(disable)
@@ -90,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     const int r = iq.next(lane);
     if (lane == 0) s_item = r;
   }
-  __syncthreads();
+  lds_barrier();
   int item = s_item;
   if (item < 0) break;
   const int pb = a.n_pblocks - 1 - (item % a.n_pblocks);  // heavy (late) rows first
@@ -163,36 +186,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const uint32_t srow_kv = uint32_t(sr) * rowk_b + kcol_b;  // this thread's first staged row, byte offset in K/V
   const uint32_t srow_id = uint32_t(sr) * 4;                // and in the ids
 
-  // Per-chunk constants kept in LDS rather than registers: the 4 pair
-  // frequencies of each 16-byte column chunk, and for each rotation kind the
-  // cos/sin of the affine id step between the two K rows a thread stages. The
-  // second K row a thread stages is RPS keys after the first; when their
-  // rotation ids differ by that step (RPS for base ids, RPS / s for remote ids
-  // when s divides RPS) its cos/sin are the first row's times the step's.
-  __shared__ uint2 kfreq[2][CPR * 4];  // [0]: base frequencies, [1]: remote frequencies
-  __shared__ float2 kstep[2][CPR * 4];
-  const int id_step1 = NU > 1 ? RPS : -1;
-  const int sdiv = static_cast<int>(a.scale_div.div);
-  const int id_step2 = (NU > 1 && RPS % sdiv == 0) ? RPS / sdiv : -1;
-  if (MODE != kNope && tid < CPR * 4) {
-    const uint32_t flo = a.f.lo[tid], fhi = a.f.hi[tid];
-    const uint32_t rlo = a.fr.lo[tid], rhi = a.fr.hi[tid];
-    kfreq[0][tid] = make_uint2(flo, fhi);
-    kfreq[1][tid] = make_uint2(rlo, rhi);
-    float s1 = 0.f, c1 = 1.f, s2 = 0.f, c2 = 1.f;
-    if (id_step1 >= 0) rope_sincos(id_step1, flo, fhi, s1, c1);
-    if (id_step2 >= 0) rope_sincos(id_step2, rlo, rhi, s2, c2);
-    kstep[0][tid] = make_float2(c1, s1);
-    kstep[1][tid] = make_float2(c2, s2);
-  }
-  __syncthreads();
-
   u32x4_t kraw[NU], vraw[NU];
   int kid[NU];
 
-  // global -> registers: this thread's K rows of tile tk and V rows of tile tv
-  // (a tile index outside [0, T) is skipped)
-  auto stage_load = [&](int tk, int tv) __attribute__((always_inline)) {
+  // Prologue staging, global -> registers: this thread's K rows (and ids) of
+  // tile tk and V rows of tile tv into the given registers (a tile index
+  // outside [0, T) is skipped)
+  auto stage_load = [&](int tk, int tv, u32x4_t(&kr)[NU], int(&ki)[NU], u32x4_t(&vr)[NU])
+                        __attribute__((always_inline)) {
     if (tk >= 0 && tk < T) {
       int p, kt;
       tile_of(tk, p, kt);
@@ -201,8 +202,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const uint32_t j = j0 + sr + RPS * u;
-        kraw[u] = bload16(kres, j * rowk_b + kcol_b);
-        kid[u] = (MODE != kNope && rot) ? bload_i32(pres, j * 4) : 0;
+        kr[u] = bload16(kres, j * rowk_b + kcol_b);
+        ki[u] = (MODE != kNope && rot) ? bload_i32(pres, j * 4) : 0;
       }
     }
     if (tv >= 0 && tv < T) {
@@ -210,12 +211,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       tile_of(tv, p, kt);
       const uint32_t j0 = uint32_t(kt) * kBN;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) vraw[u] = bload16(vres, (j0 + sr + RPS * u) * rowk_b + kcol_b);
+      for (int u = 0; u < NU; ++u) vr[u] = bload16(vres, (j0 + sr + RPS * u) * rowk_b + kcol_b);
     }
   };
 
   // registers -> LDS: K of tile tk (rotated for its pass) and V of tile tv
-  auto stage_store = [&](int tk, int tv) __attribute__((always_inline)) {
+  auto stage_store = [&](int tk, int tv, const u32x4_t(&kr)[NU], const int(&ki)[NU],
+                         const u32x4_t(&vr)[NU]) __attribute__((always_inline)) {
     if (tk >= 0 && tk < T) {
       int p, kt;
       tile_of(tk, p, kt);
@@ -231,13 +233,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
           kfhi[e] = f.y;
         }
         float cs[4], sn[4];
-        const int r0 = rot_index<MODE>(kid[0], rot, a);
+        const int r0 = rot_index<MODE>(ki[0], rot, a);
 #pragma unroll
         for (int e = 0; e < 4; ++e) rope_sincos(r0, kflo[e], kfhi[e], sn[e], cs[e]);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           if (u > 0) {
-            const int ru = rot_index<MODE>(kid[u], rot, a);
+            const int ru = rot_index<MODE>(ki[u], rot, a);
             if (id_step >= 0 && ru - r0 == id_step * u) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {  // (cs + i sn) * (step cos + i step sin)
@@ -256,20 +258,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float y0, y1;
-            rot_pair(bf16_lo(kraw[u][e]), bf16_hi(kraw[u][e]), cs[e], sn[e], y0, y1);
+            rot_pair(bf16_lo(kr[u][e]), bf16_hi(kr[u][e]), cs[e], sn[e], y0, y1);
             y[e] = pack_bf16(y0, y1);
           }
           *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = y;
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = kraw[u];
+        for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * KRow + sc * 8]) = kr[u];
       }
     }
     if (tv >= 0 && tv < T) {
       uint16_t* dst = Vs[tv & 1];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * VRow + sc * 8]) = vraw[u];
+      for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4_t*>(&dst[(sr + RPS * u) * VRow + sc * 8]) = vr[u];
     }
   };
 
@@ -281,7 +283,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // break it are redone exactly by fix_row1 after the matrix phase.
   bool need_fix = false;
   // this thread's frequencies and row steps for the rotation kind of the K
-  // tiles being staged, in registers (reloaded when that kind changes)
+  // tiles being staged, in registers (reloaded when that kind changes); the
+  // ALiBi kernels, short of registers, read them from the LDS tables instead
   uint2 kf_reg[4];
   float2 ks_reg[4];
   int kreg_rot = -1;
@@ -334,26 +337,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 
   // ---- query operand (B of S^T = K Q^T): lane holds row lr, dims ks*16 + lg*8 .. +7
   u32x4_t qreg[KS];
-  auto load_q = [&](int p) __attribute__((always_inline)) {
-    const int rot = p ? rot1 : rot0;
+  // issue the loads of this lane's query chunks and id (rows past the sequence read 0) ...
+  auto issue_q = [&](u32x4_t(&qraw)[KS], int& qid) __attribute__((always_inline)) {
     const uint32_t i = uint32_t(i0 + lr);
     const uint32_t qoff = i * rowq_b + uint32_t(h) * D * 2 + lg * 16;
-    const int r = (MODE != kNope && rot) ? rot_index<MODE>(bload_i32(pres, i * 4), rot, a) : 0;
+    qid = MODE != kNope ? bload_i32(pres, i * 4) : 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = bload16(qres, qoff + ks * 32);
+  };
+  // ... and rotate them for pass p into qreg
+  auto rotate_q = [&](int p, const u32x4_t(&qraw)[KS], int qid) __attribute__((always_inline)) {
+    const int rot = p ? rot1 : rot0;
+    const int r = (MODE != kNope && rot) ? rot_index<MODE>(qid, rot, a) : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t x = bload16(qres, qoff + ks * 32);  // rows past the sequence read 0
+      u32x4_t x = qraw[ks];
       if (MODE != kNope && rot) {
-        uint32_t flo[4], fhi[4];
-        const RopeFreq& fq = rot == 2 ? a.fr : a.f;
+        uint32_t flo[4], fhi[4];  // pair frequencies from the LDS copy of the table
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          flo[e] = fq.lo[ks * 8 + lg * 4 + e];
-          fhi[e] = fq.hi[ks * 8 + lg * 4 + e];
+          const uint2 f = kfreq[rot - 1][ks * 8 + lg * 4 + e];
+          flo[e] = f.x;
+          fhi[e] = f.y;
         }
         x = rotate_chunk(x, r, flo, fhi);
       }
       qreg[ks] = x;
     }
+  };
+  auto load_q = [&](int p) __attribute__((always_inline)) {
+    u32x4_t qraw[KS];
+    int qid;
+    issue_q(qraw, qid);
+    rotate_q(p, qraw, qid);
   };
 
   // ---- per-lane LDS addresses of the PV operand (transposing reads of V) ---
@@ -364,36 +380,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   const int vcol0 = 16 * (lr >> 4) + 4 * (j15 & 3);
 
   // ---- running statistics ---------------------------------------------------
-  f32x16_t oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  f32x16_t oacc[DB];   // set to zero after the prologue, which does not need them
   f32x16_t sacc[2];    // S^T of the tile in flight (two 32-key blocks)
   u32x4_t pop[4];      // its P, bf16, as four 16-key B operands
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) pop[kk] = u32x4_t{0, 0, 0, 0};
   float m_run = -INFINITY;  // running max of scaled scores, log2 units
   float l_run = 0.f;        // this lane's share of the running sum
   const float sl2 = a.scale_log2;
   // ALiBi slope of this wave's head in log2 units (the scores are kept in log2 units)
   const float slope2 = ALIBI ? a.alibi[h] * 1.4426950408889634f : 0.f;
 
-  // does tile t hold any kept (row, key) pair of this wave?
-  auto wave_live = [&](int t, bool& need_mask, int& dlo, int& dhi, int& j0) __attribute__((always_inline)) {
+  // does tile t hold any kept (row, key) pair of this wave? Also: do some of
+  // its pairs fall below the pass's distance range (need_lo) or above it
+  // (need_hi)?
+  auto wave_live = [&](int t, bool& need_lo, bool& need_hi, int& dlo, int& dhi, int& j0)
+                       __attribute__((always_inline)) {
     int p, kt;
     tile_of(t, p, kt);
     dlo = p ? dlo1 : dlo0;
     dhi = p ? dhi1 : dhi0;
     j0 = kt * kBN;
     const int dmin = i0 - (j0 + kBN - 1), dmax = i1 - j0;
-    need_mask = dmin < dlo || dmax > dhi;
+    need_lo = dmin < dlo;
+    need_hi = dmax > dhi;
     return i1 >= i0 && dmax >= dlo && dmin <= dhi;
   };
   auto live = [&](int t) __attribute__((always_inline)) {
-    bool nm;
+    bool nl, nh;
     int dlo, dhi, j0;
-    return wave_live(t, nm, dlo, dhi, j0);
+    return wave_live(t, nl, nh, dlo, dhi, j0);
   };
 
   auto xhalf_max = [&](float x) __attribute__((always_inline)) {
@@ -447,11 +461,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float sn, cs, y0, y1;
-      phase_sincos(phase_top(r0, kf_reg[e].x, kf_reg[e].y), sn, cs);
+      const uint2 kf = ALIBI ? kfreq[rot - 1][sc * 4 + e] : kf_reg[e];
+      phase_sincos(phase_top(r0, kf.x, kf.y), sn, cs);
       rot_pair(bf16_lo(kraw[0][e]), bf16_hi(kraw[0][e]), cs, sn, y0, y1);
       krot[0][e] = pack_bf16(y0, y1);
       if (NU > 1) {  // the second row: one id step further, (cs + i sn) * (step cos + i step sin)
-        const float2 es = ks_reg[e];
+        const float2 es = ALIBI ? kstep[rot - 1][sc * 4 + e] : ks_reg[e];
         const float c2 = cs * es.x - sn * es.y, s2 = sn * es.x + cs * es.y;
         rot_pair(bf16_lo(kraw[NU - 1][e]), bf16_hi(kraw[NU - 1][e]), c2, s2, y0, y1);
         krot[NU - 1][e] = pack_bf16(y0, y1);
@@ -468,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // (one wave reads only about a quarter of the CU's LDS rate, so the matrix
   // phase is bound by its own operand reads). The rotating modes measured
   // slower with it: their vector phase is already full.
-  constexpr bool kVpre = MODE == kNope;
+  constexpr bool kVpre = MODE == kNope && !ALIBI;
   u32x4_t vpre[kVpre ? 2 : 1][DB];
   auto read_vpre = [&](int t) __attribute__((always_inline)) {
     const uint16_t* vbase = &Vs[t & 1][vrow0 * VRow + vcol0];
@@ -545,9 +560,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 
   // vector phase of tile t: mask, online softmax, P -> bf16, lazy O rescale
   auto softmax_step = [&](int t) __attribute__((always_inline)) {
-    bool need_mask;
+    bool need_lo, need_hi;
     int dlo, dhi, j0;
-    if (!wave_live(t, need_mask, dlo, dhi, j0)) {
+    if (!wave_live(t, need_lo, need_hi, dlo, dhi, j0)) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) pop[kk] = u32x4_t{0, 0, 0, 0};
       rotate_k(t);
@@ -564,14 +579,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
           sacc[nb][r] = fmaf(sacc[nb][r], sl2, fmaf(slope2, c, b0));
         }
     }
-    if (need_mask) {
+    // Keep dlo <= i - j <= dhi, i.e. dbase - dhi <= c <= dbase - dlo for the key
+    // offset c = j - j0 - 4 lg of a register, a constant: each bound that cuts
+    // the tile costs one compare and one select per score. (A live tile has
+    // dlo <= S and dhi >= -S, so neither difference overflows.)
+    if (need_lo) {
+      const int chi = dbase - dlo;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dist = dbase - (nb * 32 + 8 * (r >> 2) + (r & 3));
-          if (dist < dlo || dist > dhi) sacc[nb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (nb * 32 + 8 * (r >> 2) + (r & 3) > chi) sacc[nb][r] = -INFINITY;
+    }
+    if (need_hi) {
+      const int clo = dbase - dhi;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (nb * 32 + 8 * (r >> 2) + (r & 3) < clo) sacc[nb][r] = -INFINITY;
     }
     float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
@@ -617,11 +643,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     return true;
   };
 
-  // ---- prologue: K tile 0 in LDS; K tile 1 and V tile 0 in registers --------
-  stage_load(0, -1);
-  stage_store(0, -1);
-  stage_load(1, 0);
-  load_q(pass_of(0));
+  // ---- prologue: one round of global loads (K tiles 0 and 1 with their ids,
+  // V tile 0, the queries, then K tile 2 and V tile 1 into the loop's staging
+  // registers, in the loop's issue order so its waits stay exact), then K
+  // tiles 0 and 1 and V tile 0 to LDS and the query rotation
+  {
+    u32x4_t kraw0[NU], kraw1[NU], vraw0[NU], qraw[KS];
+    int kid0[NU], kid1[NU], qid;
+    stage_load(0, 0, kraw0, kid0, vraw0);
+    stage_load(1, -1, kraw1, kid1, vraw0);
+    issue_q(qraw, qid);
+    stage_load_nb(2, 1);
+    stage_store(0, 0, kraw0, kid0, vraw0);
+    stage_store(1, -1, kraw1, kid1, vraw0);
+    rotate_q(pass_of(0), qraw, qid);
+  }
   lds_barrier();
 
   // ---- phases -----------------------------------------------------------------
@@ -633,12 +669,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // issues the loads of K tile t+3 and V tile t+2.
   if (group == 1) lds_barrier();
   qk_or_clear(0);
-  stage_store(1, 0);
-  stage_load_nb(2, 1);  // same issue order as in the loop, so the loads keep exact wait counts
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) pop[kk] = u32x4_t{0, 0, 0, 0};
   lds_barrier();
 #pragma clang loop unroll(disable)
   for (int t = 0; t < T; ++t) {
-    if (MODE != kNope) {
+    if (MODE != kNope && !ALIBI) {
       const int srot = pass_of(t + 2) ? rot1 : rot0;
       if (srot != kreg_rot) load_kregs(srot);
     }
@@ -660,28 +700,41 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   if (group == 0) lds_barrier();
 
   // ---- finalize ---------------------------------------------------------------
+  // O / l goes through LDS so that each global store writes whole rows: a
+  // lane's accumulators hold 4 dims of one row, which stored directly would
+  // touch 32 rows per instruction. Both groups have passed their last loop
+  // barrier, so the K and V tiles are free: waves 0-3 use the K buffers, waves
+  // 4-7 the V buffers, 32 rows of D + 8 elements each (16-byte aligned rows).
+  const float l = l_run + __shfl_xor(l_run, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  constexpr int ORow = D + 8;
+  static_assert(4 * 32 * ORow <= 2 * kBN * KRow && 4 * 32 * ORow <= 2 * kBN * VRow, "output staging fits");
+  uint16_t* ob = (group == 0 ? &Ks[0][0] : &Vs[0][0]) + (wave & 3) * 32 * ORow;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      u32x2_t w;
+      w[0] = pack_bf16(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
+      w[1] = pack_bf16(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(ob + lr * ORow + db * 32 + 8 * g4 + 4 * lg) = w;
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's rows are in LDS
   uint16_t* og = static_cast<uint16_t*>(a.o) + size_t(b) * S * a.Hq * D + size_t(h) * D;
   const size_t rowq = size_t(a.Hq) * D;
-  const float l = l_run + __shfl_xor(l_run, 32);
-  const int i = i0 + lr;
-  if (i <= i1) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+  constexpr int RPI = 64 / CPR;  // rows per read / store instruction
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * lg;
-        u32x2_t w;
-        w[0] = pack_bf16(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
-        w[1] = pack_bf16(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(og + size_t(i) * rowq + d) = w;
-      }
-    if (a.lse && lg == 0) {
-      const float lse = l > 0.f ? (m_run + log2f(l)) * 0.6931471805599453f : -INFINITY;
-      a.lse[(size_t(b) * a.Hq + h) * S + i] = lse;
-    }
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rr = it * RPI + lane / CPR, ch = lane % CPR;
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ob + rr * ORow + ch * 8);
+    if (i0 + rr <= i1) *reinterpret_cast<u32x4_t*>(og + size_t(i0 + rr) * rowq + ch * 8) = x;
   }
-  __syncthreads();  // LDS and s_item are reused by the next item
+  const int i = i0 + lr;
+  if (a.lse && lg == 0 && i <= i1) {
+    const float lse = l > 0.f ? (m_run + log2f(l)) * 0.6931471805599453f : -INFINITY;
+    a.lse[(size_t(b) * a.Hq + h) * S + i] = lse;
+  }
+  lds_barrier();  // LDS and s_item are reused by the next item (the output stores need no wait)
   }  // items
 
   if (wave == 0) iq.finish(lane);
