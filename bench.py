@@ -117,7 +117,72 @@ def time_launches(fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps, wall
 
 
-def bench_prefill(name, steps, warmup, unfused=False, min_seconds=0.0):
+def item_trace_summary(step, launches=50):
+    """Item phases of the bf16 prefill kernel from a trace build
+    (`python -m position_remapped_rope_amd.build --trace OUT.so`, loaded with
+    PROPE_LIB_PATH=OUT.so): `launches` back-to-back launches, then the
+    timestamps of the last one, per workgroup and item, as medians in us. The
+    kernel's 100 MHz real-time counter gives 10 ns resolution."""
+    import ctypes
+    import numpy as np
+    import torch
+    import position_remapped_rope_amd as P
+    L = P.lib()
+    if not hasattr(L, "prope_item_trace_read"):
+        raise SystemExit("--item-trace needs the trace build: python -m position_remapped_rope_amd.build "
+                         "--trace OUT.so, then PROPE_LIB_PATH=OUT.so")
+    L.prope_item_trace_read.restype = ctypes.c_int
+    L.prope_item_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    wgs, slots = 1024, 64
+    buf = np.zeros(wgs * slots, dtype=np.uint64)
+    torch.cuda.synchronize()
+    assert L.prope_item_trace_read(buf.ctypes.data, buf.nbytes) == 0  # clears the table
+    for i in range(launches):
+        step(i)
+    torch.cuda.synchronize()
+    assert L.prope_item_trace_read(buf.ctypes.data, buf.nbytes) == 0
+    return {"launches": launches, **summarize_item_trace(buf.reshape(wgs, slots))}
+
+
+def summarize_item_trace(table, per_item=5):
+    """Medians (us) of the item phases in an item-trace table: one row per
+    workgroup of 100 MHz counter values, slot 0 at entry, slots 1 + 5k .. 5 + 5k
+    for item k (start after the claim, end of the load and rotation setup,
+    start of the tile loop, end of the loop, end of the item) and the last slot
+    at exit; zero where nothing was recorded. non_loop_share is the part of the
+    time from entry to the end of the last traced item spent outside tile
+    loops (launch ramp, setup, prologue, finalize, claims)."""
+    import numpy as np
+    tr = np.asarray(table).astype(np.int64)
+    slots = tr.shape[1]
+    used = tr[:, 0] > 0
+    tr = tr[used]
+    t0 = tr[:, 0].min()
+    us = lambda x: float(x) / 100.0
+    names = ("setup", "prologue", "loop", "finalize")
+    phases = {n: [] for n in names}
+    gaps, overhead_share = [], []
+    for r in tr:
+        items = [r[1 + per_item * k: 1 + per_item * (k + 1)] for k in range((slots - 2) // per_item)]
+        items = [it for it in items if (it > 0).all()]
+        busy_loop = 0
+        for k, it in enumerate(items):
+            for n, d in zip(names, np.diff(it)):
+                phases[n].append(us(d))
+            busy_loop += it[3] - it[2]
+            if k + 1 < len(items):
+                gaps.append(us(items[k + 1][0] - it[4]))
+        if items:  # share of the time from entry to the end of the last traced item
+            overhead_share.append(1.0 - busy_loop / float(items[-1][4] - r[0]))
+    med = lambda v: round(float(np.median(v)), 3) if v else None
+    return {"workgroups": int(used.sum()), "items_traced": len(phases["loop"]),
+            "median_us": {**{n: med(v) for n, v in phases.items()}, "claim_gap": med(gaps)},
+            "launch_span_us": round(us(tr[:, slots - 1].max() - t0), 2),
+            "workgroup_exit_us": [round(us(np.percentile(tr[:, slots - 1] - t0, q)), 2) for q in (0, 50, 100)],
+            "non_loop_share_median": med(overhead_share)}
+
+
+def bench_prefill(name, steps, warmup, unfused=False, min_seconds=0.0, item_trace=False):
     import torch
     import position_remapped_rope_amd as P
     import workloads as W
@@ -149,7 +214,10 @@ def bench_prefill(name, steps, warmup, unfused=False, min_seconds=0.0):
     flops = prefill_flops(w)
     tflops = flops / (avg * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
-    return w, inp, dict(avg_ms=avg, steps_timed=steps, flops=flops, tflops=tflops, frac=tflops / peak)
+    r = dict(avg_ms=avg, steps_timed=steps, flops=flops, tflops=tflops, frac=tflops / peak)
+    if item_trace:
+        r["item_trace"] = item_trace_summary(step, launches=max(2, min(50, int(200.0 / max(avg, 1e-3)))))
+    return w, inp, r
 
 
 def bench_decode(name, steps, warmup, S=None):
@@ -280,6 +348,8 @@ def main():
                                        "nope_global_8k", "endprompt_fp32", "decode_b1", "decode_b8", "rope_apply",
                                        "copy"],
                     help="time one leg only and print its figures (for profiler runs)")
+    ap.add_argument("--item-trace", action="store_true",
+                    help="with --only on a bf16 prefill leg and a trace build: per-item phase times")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on a single GPU (no multi-GPU path); --gpus must be 1"}))
@@ -299,10 +369,12 @@ def main():
             r = bench_rope_apply(args.steps, args.warmup)
         elif args.only in ("prope_local_8k", "nope_global_8k", "endprompt_fp32"):
             name = args.only
-            _, _, r = bench_prefill(name, args.steps, args.warmup, min_seconds=0.1)
+            _, _, r = bench_prefill(name, args.steps, args.warmup, min_seconds=0.1,
+                                    item_trace=args.item_trace and name != "endprompt_fp32")
         elif args.only.startswith("prefill"):
             name = "bifocal_128k" if args.only == "prefill_128k" else "bifocal_64k"
-            _, _, r = bench_prefill(name, args.steps, args.warmup, unfused=args.only.endswith("unfused"))
+            _, _, r = bench_prefill(name, args.steps, args.warmup, unfused=args.only.endswith("unfused"),
+                                    item_trace=args.item_trace and not args.only.endswith("unfused"))
         else:
             name = "bifocal_decode_128k_b1" if args.only == "decode_b1" else "bifocal_decode_128k_b8"
             r = bench_decode(name, args.steps, args.warmup)

@@ -1,11 +1,16 @@
 """Build libprope.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m position_remapped_rope_amd.build [-v] [--sanitize OUT.so]
+Usage: python -m position_remapped_rope_amd.build [-v] [--sanitize OUT.so | --trace OUT.so]
 
 --sanitize builds a copy whose host code (argument checks, launch set-up,
 integer helpers) carries AddressSanitizer and UndefinedBehaviorSanitizer; the
 device code is built as usual. Load it with the ASan runtime preloaded
 (libclang_rt.asan-x86_64.so), for CPU-side tests.
+
+--trace builds a copy whose bf16 prefill kernel records item-phase timestamps
+(PROPE_ITEM_TRACE=1) and exports prope_item_trace_read; `bench.py --only LEG
+--item-trace` run with PROPE_LIB_PATH=OUT.so summarises them. Not for
+production use: the timestamps cost a few instructions per item.
 """
 from __future__ import annotations
 
@@ -71,12 +76,19 @@ def _compile(src: str, verbose: bool, build_dir: str = BUILD_DIR, extra=()) -> s
     return obj
 
 
-def build(verbose: bool = False, sanitize_out: str = "") -> str:
+TRACE_FLAGS = ["-DPROPE_ITEM_TRACE=1"]
+
+
+def build(verbose: bool = False, sanitize_out: str = "", trace_out: str = "") -> str:
     """Compile every source (in parallel) and link libprope.so; returns its path.
-    With sanitize_out, link a host-sanitized copy there instead."""
-    build_dir = os.path.join(BUILD_DIR, "asan") if sanitize_out else BUILD_DIR
-    extra = SANITIZE_FLAGS if sanitize_out else []
-    out = sanitize_out or OUT
+    With sanitize_out, link a host-sanitized copy there instead; with
+    trace_out, a copy with item-phase tracing."""
+    if sanitize_out and trace_out:
+        raise ValueError("choose one of sanitize_out and trace_out")
+    build_dir = os.path.join(BUILD_DIR, "asan") if sanitize_out else \
+        os.path.join(BUILD_DIR, "trace") if trace_out else BUILD_DIR
+    extra = SANITIZE_FLAGS if sanitize_out else TRACE_FLAGS if trace_out else []
+    out = sanitize_out or trace_out or OUT
     os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
@@ -94,4 +106,5 @@ def build(verbose: bool = False, sanitize_out: str = "") -> str:
 
 if __name__ == "__main__":
     san = sys.argv[sys.argv.index("--sanitize") + 1] if "--sanitize" in sys.argv else ""
-    print(build(verbose="-v" in sys.argv, sanitize_out=san))
+    tr = sys.argv[sys.argv.index("--trace") + 1] if "--trace" in sys.argv else ""
+    print(build(verbose="-v" in sys.argv, sanitize_out=san, trace_out=tr))

@@ -52,8 +52,31 @@
 
 #include "prefill_common.hpp"
 
+// Item-phase tracing, compiled in only by the trace build (PROPE_ITEM_TRACE=1):
+// thread 0 of each of the first kTraceWGs workgroups records the 100 MHz
+// real-time counter at entry (slot 0), at five points of each of its first
+// kTraceItems items (slots 1 + 5k ...: start after the claim, end of the load
+// and rotation setup, start of the tile loop, end of the loop, end of the
+// item) and at exit (slot 63).
+#ifndef PROPE_ITEM_TRACE
+#define PROPE_ITEM_TRACE 0
+#endif
+
 namespace prope {
+constexpr int kTraceWGs = 1024, kTraceSlots = 64, kTraceItems = 12;
+#if PROPE_ITEM_TRACE
+__device__ unsigned long long item_trace[kTraceWGs * kTraceSlots];
+#endif
 namespace {
+
+__device__ __forceinline__ void trace_point(int slot) {
+#if PROPE_ITEM_TRACE
+  if (threadIdx.x == 0 && blockIdx.x < kTraceWGs && slot < kTraceSlots)
+    item_trace[blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
+#else
+  (void)slot;
+#endif
+}
 
 using namespace pf;
 
@@ -107,6 +130,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // (the barrier after each claim also publishes the tables above)
   ItemQueue iq(a);
   __shared__ int s_item;
+  trace_point(0);
+  int n_traced = 0;  // items of this workgroup so far (trace build)
+  auto trace_item = [&](int k) __attribute__((always_inline)) {
+    if (n_traced < kTraceItems) trace_point(1 + 5 * n_traced + k);
+  };
 #pragma clang loop unroll(disable)
   for (;;) {
   if (wave == 0) {
@@ -116,6 +144,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   lds_barrier();
   int item = s_item;
   if (item < 0) break;
+  trace_item(0);
   const int pb = a.n_pblocks - 1 - (item % a.n_pblocks);  // heavy (late) rows first
   item /= a.n_pblocks;
   const int hsub = item % a.n_hsub;
@@ -667,6 +696,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // also rotates this wave's rows of K tile t+2; the matrix phase after it
   // stores them and its rows of V tile t+1 to LDS between its MFMAs, then
   // issues the loads of K tile t+3 and V tile t+2.
+  trace_item(1);
   if (group == 1) lds_barrier();
   qk_or_clear(0);
 #pragma unroll
@@ -676,6 +706,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) pop[kk] = u32x4_t{0, 0, 0, 0};
   lds_barrier();
+  trace_item(2);
 #pragma clang loop unroll(disable)
   for (int t = 0; t < T; ++t) {
     if (MODE != kNope && !ALIBI) {
@@ -698,6 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     lds_barrier();
   }
   if (group == 0) lds_barrier();
+  trace_item(3);
 
   // ---- finalize ---------------------------------------------------------------
   // O / l goes through LDS so that each global store writes whole rows: a
@@ -735,9 +767,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     a.lse[(size_t(b) * a.Hq + h) * S + i] = lse;
   }
   lds_barrier();  // LDS and s_item are reused by the next item (the output stores need no wait)
+  trace_item(4);
+  ++n_traced;
   }  // items
 
   if (wave == 0) iq.finish(lane);
+  trace_point(kTraceSlots - 1);
 }
 
 int64_t n_items(const PrefillArgs& a) { return int64_t(a.B) * a.Hkv * a.n_hsub * a.n_pblocks; }
@@ -774,3 +809,17 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace prope
+
+#if PROPE_ITEM_TRACE
+// Trace build only (not part of the library's ABI): copy the item-phase table
+// (kTraceWGs x kTraceSlots 64-bit counters, zero where nothing was recorded)
+// to host memory and clear it. dst must hold sizeof the table; returns 0, or
+// the HIP error of the copy.
+extern "C" int prope_item_trace_read(void* dst, size_t bytes) {
+  if (bytes < sizeof(prope::item_trace)) return hipErrorInvalidValue;
+  hipError_t e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(prope::item_trace), sizeof(prope::item_trace));
+  if (e != hipSuccess) return e;
+  static unsigned long long zero[prope::kTraceWGs * prope::kTraceSlots];
+  return hipMemcpyToSymbol(HIP_SYMBOL(prope::item_trace), zero, sizeof(zero));
+}
+#endif

@@ -47,3 +47,30 @@ def test_no_kernel_spills_to_scratch(tmp_path):
             assert sc == 0, f"{src}: {n} uses {sc} bytes of scratch per lane"
         seen += len(names)
     assert seen >= 20
+
+
+def test_item_trace_summary_phases():
+    """bench.py's item-trace summary on a synthetic table: two workgroups, two
+    items each, known phase lengths (100 counter ticks = 1 us)."""
+    import sys
+    import numpy as np
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    t = np.zeros((4, 64), dtype=np.uint64)
+    for w, base in ((0, 1000), (1, 1050)):
+        t[w, 0] = base
+        x = base + 100  # claim of item 0 done at +1 us
+        for k in range(2):
+            # setup 3 us, prologue 1 us, loop 20 us, finalize 1.5 us, then a 0.5 us claim gap
+            pts = [x, x + 300, x + 400, x + 2400, x + 2550]
+            t[w, 1 + 5 * k: 6 + 5 * k] = pts
+            x = pts[-1] + 50
+        t[w, 63] = x + 10
+    s = bench.summarize_item_trace(t)
+    assert s["workgroups"] == 2 and s["items_traced"] == 4
+    m = s["median_us"]
+    assert (m["setup"], m["prologue"], m["loop"], m["finalize"], m["claim_gap"]) == (3.0, 1.0, 20.0, 1.5, 0.5)
+    # each workgroup: entry to the end of its last item = 1 + 25.5 + 0.5 + 25.5 = 52.5 us, 40 us of it in
+    # the tile loops; exit 0.6 us later; the second workgroup starts 0.5 us after the first
+    assert abs(s["non_loop_share_median"] - (1 - 40 / 52.5)) < 1e-3  # reported to 3 decimals
+    assert s["launch_span_us"] == 53.6 and s["workgroup_exit_us"] == [53.1, 53.35, 53.6]
