@@ -90,6 +90,7 @@ def build(verbose: bool = False, sanitize_out: str = "", trace_out: str = "") ->
     extra = SANITIZE_FLAGS if sanitize_out else TRACE_FLAGS if trace_out else []
     out = sanitize_out or trace_out or OUT
     os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
     tmp = out + ".tmp"
