@@ -74,3 +74,26 @@ def test_item_trace_summary_phases():
     # the tile loops; exit 0.6 us later; the second workgroup starts 0.5 us after the first
     assert abs(s["non_loop_share_median"] - (1 - 40 / 52.5)) < 1e-3  # reported to 3 decimals
     assert s["launch_span_us"] == 53.6 and s["workgroup_exit_us"] == [53.1, 53.35, 53.6]
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+def test_trace_build_compiles_and_exports_reader(tmp_path):
+    """The item-phase trace build (build.py --trace) of the bf16 prefill keeps
+    compiling, defines prope_item_trace_read, and the default build does not."""
+    import sys
+    sys.path.insert(0, ROOT)
+    from position_remapped_rope_amd import build as b
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    src = os.path.join(CSRC, "prefill_bf16.hip")
+    syms = {}
+    for tag, extra in (("trace", b.TRACE_FLAGS), ("default", [])):
+        obj = tmp_path / f"prefill_{tag}.o"
+        r = subprocess.run([hipcc, *b.FLAGS, *extra, "-x", "hip", "-fno-honor-nans", "-c", src, "-o", str(obj)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        nm = subprocess.run(["nm", "-g", "--defined-only", str(obj)], capture_output=True, text=True)
+        assert nm.returncode == 0, nm.stderr
+        syms[tag] = nm.stdout
+    assert "prope_item_trace_read" in syms["trace"]
+    assert "prope_item_trace_read" not in syms["default"]
