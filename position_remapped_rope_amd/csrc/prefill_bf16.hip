@@ -205,6 +205,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     p = pass_of(t);
     kt = p ? tb1 + (t - tc0) : tb0 + t;
   };
+  // Are the rotation indices of a thread's two staged K rows (ids k0 and k1,
+  // RPS keys apart, k0's index r0) one id step apart? With a period the indices
+  // themselves are compared (they wrap at P). Otherwise it is enough that the
+  // ids are RPS apart without wrapping around the int32 range: for remote ids
+  // floor(p/s), s divides RPS wherever id_step >= 0.
+  auto rows_affine = [&](int k0, int k1, int r0, int rot, int id_step) __attribute__((always_inline)) {
+    if (id_step < 0) return false;
+    if (MODE == kRope && a.period > 0) return rot_index<MODE>(k1, rot, a) - r0 == id_step;
+    return k1 > k0 && uint32_t(k1) - uint32_t(k0) == uint32_t(RPS);
+  };
 
   // ---- per-thread staging coordinates --------------------------------------
   // group g stages rows [HR*g, HR*g + HR) of every K and V tile
@@ -268,8 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           if (u > 0) {
-            const int ru = rot_index<MODE>(ki[u], rot, a);
-            if (id_step >= 0 && ru - r0 == id_step * u) {
+            if (rows_affine(ki[0], ki[u], r0, rot, id_step)) {  // (NU = 2: u = 1)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {  // (cs + i sn) * (step cos + i step sin)
                 const float2 es = kstep[rot - 1][sc * 4 + e];
@@ -279,6 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
                 sn[e] = s2;
               }
             } else {
+              const int ru = rot_index<MODE>(ki[u], rot, a);
 #pragma unroll
               for (int e = 0; e < 4; ++e) rope_sincos(ru, kflo[e], kfhi[e], sn[e], cs[e]);
             }
@@ -486,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     const int rot = pk ? rot1 : rot0;
     const int id_step = rot == 2 ? id_step2 : id_step1;
     const int r0 = rot_index<MODE>(kid[0], rot, a);
-    if (NU > 1) need_fix = !(id_step >= 0 && rot_index<MODE>(kid[NU - 1], rot, a) - r0 == id_step);
+    if (NU > 1) need_fix = !rows_affine(kid[0], kid[NU - 1], r0, rot, id_step);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float sn, cs, y0, y1;

@@ -63,6 +63,15 @@ NEG = [
      dict(rope_base=1e6, remap_scale=2, window_left=50, remote_map="interp"), -260),
     ("fp32_rope_period", (1, 120, 4, 2, 64, "fp32"), "rope", dict(rope_base=1e4, period=16, window_left=30), -70),
     ("fp32_bifocal", (1, 150, 4, 2, 128, "fp32"), "bifocal", dict(rope_base=1e6, remap_scale=3, window_left=20), -77),
+    # ids that run past INT32_MAX and wrap to INT32_MIN mid-sequence: two K rows a
+    # thread stages 16 keys apart can then have ids 16 apart modulo 2^32 only,
+    # which must not be taken for an affine step
+    ("rope_ids_wrap_int32", (1, 300, 4, 2, 128, "bf16"), "rope", dict(rope_base=1e4), (1 << 31) - 150),
+    ("bifocal_ids_wrap_int32", (1, 400, 4, 2, 128, "bf16"), "bifocal",
+     dict(rope_base=1e6, remap_scale=2, window_left=64), (1 << 31) - 200),
+    ("bifocal_interp_ids_wrap_int32", (1, 300, 4, 2, 64, "bf16"), "bifocal",
+     dict(rope_base=1e6, remap_scale=2, window_left=40, remote_map="interp"), (1 << 31) - 120),
+    ("fp32_rope_ids_wrap_int32", (1, 100, 4, 2, 64, "fp32"), "rope", dict(rope_base=1e4), (1 << 31) - 50),
 ]
 
 
