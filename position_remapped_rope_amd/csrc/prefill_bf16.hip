@@ -48,6 +48,7 @@
 // the other wave's vector work. K and V tiles are double-buffered in LDS; each
 // group stages half of every tile's rows, with the global loads issued one
 // phase pair ahead.
+#include <float.h>
 #include <limits.h>
 
 #include "prefill_common.hpp"
@@ -422,7 +423,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   f32x16_t oacc[DB];   // set to zero after the prologue, which does not need them
   f32x16_t sacc[2];    // S^T of the tile in flight (two 32-key blocks)
   u32x4_t pop[4];      // its P, bf16, as four 16-key B operands
-  float m_run = -INFINITY;  // running max of scaled scores, log2 units
+  // Reference max of the scaled scores (log2 units) that P is taken against.
+  // It starts at -FLT_MAX rather than -inf, so that it is always a finite
+  // reference: the first kept key of a row raises it to that tile's max (and the
+  // rescale of the empty O and l by 2^(-FLT_MAX - max) is a multiply by 0), and a
+  // row with no kept key yet takes P = 2^-inf = 0.
+  float m_run = -FLT_MAX;
   float l_run = 0.f;        // this lane's share of the running sum
   const float sl2 = a.scale_log2;
   // ALiBi slope of this wave's head in log2 units (the scores are kept in log2 units)
@@ -501,7 +507,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     for (int e = 0; e < 4; ++e) {
       float sn, cs, y0, y1;
       const uint2 kf = ALIBI ? kfreq[rot - 1][sc * 4 + e] : kf_reg[e];
-      phase_sincos(phase_top(r0, kf.x, kf.y), sn, cs);
+      {  // The phase's top 23 bits as the mantissa of a float x in [1, 2): the
+         // sine and cosine take revolutions, so x is the same angle (one
+         // instruction instead of a conversion and a scaling; the truncation
+         // moves the angle by under 2^-23 turn, far below the bf16 rounding of
+         // the rotated key)
+        const float x = __uint_as_float(__builtin_amdgcn_alignbit(0x7fu, phase_top(r0, kf.x, kf.y), 9));
+        sn = __builtin_amdgcn_sinf(x);
+        cs = __builtin_amdgcn_cosf(x);
+      }
       rot_pair(bf16_lo(kraw[0][e]), bf16_hi(kraw[0][e]), cs, sn, y0, y1);
       krot[0][e] = pack_bf16(y0, y1);
       if (NU > 1) {  // the second row: one id step further, (cs + i sn) * (step cos + i step sin)
@@ -638,31 +652,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         for (int r = 0; r < 16; ++r)
           if (nb * 32 + 8 * (r >> 2) + (r & 3) < clo) sacc[nb][r] = -INFINITY;
     }
-    float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[1][0], sacc[1][1]);
+    // the row max of this lane's 32 scores in 16 three-input maxima
+    auto max3 = [](float x, float y, float z) __attribute__((always_inline)) { return fmaxf(fmaxf(x, y), z); };
+    float m1[10];
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-      mx0 = fmaxf(mx0, fmaxf(sacc[0][r], sacc[0][r + 1]));
-      mx1 = fmaxf(mx1, fmaxf(sacc[1][r], sacc[1][r + 1]));
+    for (int g = 0; g < 10; ++g) {
+      const int v = 3 * g;
+      m1[g] = max3(sacc[v >> 4][v & 15], sacc[(v + 1) >> 4][(v + 1) & 15], sacc[(v + 2) >> 4][(v + 2) & 15]);
     }
+    const float m2 = max3(max3(m1[0], m1[1], m1[2]), max3(m1[3], m1[4], m1[5]), max3(m1[6], m1[7], m1[8]));
     // sl2 > 0, so scaling after the max is the max of the scaled scores
     const float smul = ALIBI ? 1.f : sl2;  // ALiBi scores are scaled already
-    const float mx = xhalf_max(fmaxf(mx0, mx1)) * smul;
+    const float mx = xhalf_max(fmaxf(m2, max3(m1[9], sacc[1][14], sacc[1][15]))) * smul;
     rotate_k(t);
     // The reference max moves only when the tile's max exceeds it by more than
     // 8 (log2 units): P <= 2^8 stays exact in bf16 and fp32, and O and l are
     // rescaled far less often. The final O / l and LSE = m + log2 l are unchanged.
-    const float mnew = mx > m_run + 8.f ? mx : m_run;
-    const bool grow = mnew > m_run;
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mref);
-    m_run = mnew;
+    if (__any(mx > m_run + 8.f)) {  // some row of the wave raises its reference
+      const float mnew = mx > m_run + 8.f ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+      m_run = mnew;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int nb = kk >> 1, r0 = (kk & 1) * 8;
       float pv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r0 + e], smul, -mref));
+      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r0 + e], smul, -m_run));
       const u32x4_t w = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
                          pack_bf16(pv[6], pv[7])};
       pop[kk] = w;
@@ -672,13 +694,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       rs0 = add_bf16_pair(w[2], rs0);
       rs1 = add_bf16_pair(w[3], rs1);
     }
-    l_run = l_run * alpha + (rs0 + rs1);
-    if (__any(grow)) {  // rescale O only when some row of the wave raised its max
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
+    l_run += rs0 + rs1;
     return true;
   };
 
