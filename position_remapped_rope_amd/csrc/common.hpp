@@ -32,6 +32,23 @@ __device__ __forceinline__ uint32_t phase_top(int32_t r, uint32_t flo, uint32_t 
   return __umulhi(ru, flo) + ru * fhi - (flo & sgn);
 }
 
+// The same phase from F split with a SIGNED low half: F = fhs * 2^32 + fls, fls
+// in [-2^31, 2^31) (fls = flo - 2^32 and fhs = fhi + 1 when flo >= 2^31). Then
+// the signed 64-bit product r * fls carries the sign of r by itself, and the top
+// 32 bits of (r * F) mod 2^64 are r * fhs + hi32(r * fls): one signed high
+// multiply, one low multiply and an add, no sign correction.
+struct PhaseSplit {
+  uint32_t fls;  // the signed low half, as bits
+  uint32_t fhs;
+};
+__host__ __device__ inline PhaseSplit phase_split(uint32_t flo, uint32_t fhi) {
+  return PhaseSplit{flo, fhi + (flo >> 31)};
+}
+__host__ __device__ inline uint32_t phase_top_split(int32_t r, uint32_t fls, uint32_t fhs) {
+  const int32_t hi = static_cast<int32_t>((int64_t(r) * int64_t(static_cast<int32_t>(fls))) >> 32);
+  return static_cast<uint32_t>(hi) + static_cast<uint32_t>(r) * fhs;
+}
+
 // sin and cos of 2*pi*t for t in [-1/2, 1/2) (v_sin_f32 / v_cos_f32 take revolutions).
 __device__ __forceinline__ void sincos_turns(float t, float& s, float& c) {
   s = __builtin_amdgcn_sinf(t);
@@ -51,6 +68,11 @@ __device__ __forceinline__ void phase_sincos(uint32_t ph, float& s, float& c) {
 __device__ __forceinline__ void rope_sincos(int32_t r, uint32_t flo, uint32_t fhi, float& s,
                                             float& c) {
   sincos_turns(phase_turns(r, flo, fhi), s, c);
+}
+
+// rope_sincos from the signed split of F (phase_split)
+__device__ __forceinline__ void rope_sincos_split(int32_t r, uint32_t fls, uint32_t fhs, float& s, float& c) {
+  sincos_turns(static_cast<float>(static_cast<int32_t>(phase_top_split(r, fls, fhs))) * 0x1p-32f, s, c);
 }
 
 // ---- bf16 bit helpers ---------------------------------------------------

@@ -111,16 +111,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // second K row a thread stages is RPS keys after the first; when their
   // rotation ids differ by that step (RPS for base ids, RPS / s for remote ids
   // when s divides RPS) its cos/sin are the first row's times the step's.
+  // The frequencies are held in the signed split of phase_split (one
+  // instruction less per phase); the ALiBi kernels, which read them from LDS in
+  // the loop and have fewer registers to spare, keep the plain split.
   __shared__ uint2 kfreq[2][CPR * 4];  // [0]: base frequencies, [1]: remote frequencies
   __shared__ float2 kstep[2][CPR * 4];
+  constexpr bool kSplit = !ALIBI;
+  auto kphase = [](int r, uint2 f) __attribute__((always_inline)) {
+    return kSplit ? phase_top_split(r, f.x, f.y) : phase_top(r, f.x, f.y);
+  };
+  auto ksincos = [](int r, uint2 f, float& sn, float& cs) __attribute__((always_inline)) {
+    if (kSplit) rope_sincos_split(r, f.x, f.y, sn, cs);
+    else rope_sincos(r, f.x, f.y, sn, cs);
+  };
   const int id_step1 = NU > 1 ? RPS : -1;
   const int sdiv = static_cast<int>(a.scale_div.div);
   const int id_step2 = (NU > 1 && RPS % sdiv == 0) ? RPS / sdiv : -1;
   if (MODE != kNope && tid < CPR * 4) {
     const uint32_t flo = a.f.lo[tid], fhi = a.f.hi[tid];
     const uint32_t rlo = a.fr.lo[tid], rhi = a.fr.hi[tid];
-    kfreq[0][tid] = make_uint2(flo, fhi);
-    kfreq[1][tid] = make_uint2(rlo, rhi);
+    const PhaseSplit sb = phase_split(flo, fhi), sm = phase_split(rlo, rhi);
+    kfreq[0][tid] = kSplit ? make_uint2(sb.fls, sb.fhs) : make_uint2(flo, fhi);
+    kfreq[1][tid] = kSplit ? make_uint2(sm.fls, sm.fhs) : make_uint2(rlo, rhi);
     float s1 = 0.f, c1 = 1.f, s2 = 0.f, c2 = 1.f;
     if (id_step1 >= 0) rope_sincos(id_step1, flo, fhi, s1, c1);
     if (id_step2 >= 0) rope_sincos(id_step2, rlo, rhi, s2, c2);
@@ -265,17 +277,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       const int rot = p ? rot1 : rot0;
       if (MODE != kNope && rot) {
         const int id_step = rot == 2 ? id_step2 : id_step1;
-        uint32_t kflo[4], kfhi[4];
+        uint2 kf[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint2 f = kfreq[rot - 1][sc * 4 + e];
-          kflo[e] = f.x;
-          kfhi[e] = f.y;
-        }
+        for (int e = 0; e < 4; ++e) kf[e] = kfreq[rot - 1][sc * 4 + e];
         float cs[4], sn[4];
         const int r0 = rot_index<MODE>(ki[0], rot, a);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rope_sincos(r0, kflo[e], kfhi[e], sn[e], cs[e]);
+        for (int e = 0; e < 4; ++e) ksincos(r0, kf[e], sn[e], cs[e]);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           if (u > 0) {
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
             } else {
               const int ru = rot_index<MODE>(ki[u], rot, a);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) rope_sincos(ru, kflo[e], kfhi[e], sn[e], cs[e]);
+              for (int e = 0; e < 4; ++e) ksincos(ru, kf[e], sn[e], cs[e]);
             }
           }
           u32x4_t y;
@@ -327,14 +335,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // ALiBi kernels, short of registers, read them from the LDS tables instead
   uint2 kf_reg[4];
   float2 ks_reg[4];
-  int kreg_rot = -1;
   auto load_kregs = [&](int rot) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       kf_reg[e] = kfreq[rot - 1][sc * 4 + e];
       ks_reg[e] = kstep[rot - 1][sc * 4 + e];
     }
-    kreg_rot = rot;
   };
   auto stage_load_nb = [&](int tk, int tv) __attribute__((always_inline)) {
     int p, kt;
@@ -365,9 +371,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       u32x4_t y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint2 f = kfreq[rot - 1][sc * 4 + e];
         float sn, cs, y0, y1;
-        rope_sincos(ru, f.x, f.y, sn, cs);
+        ksincos(ru, kfreq[rot - 1][sc * 4 + e], sn, cs);
         rot_pair(bf16_lo(kraw[NU - 1][e]), bf16_hi(kraw[NU - 1][e]), cs, sn, y0, y1);
         y[e] = pack_bf16(y0, y1);
       }
@@ -393,14 +398,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t x = qraw[ks];
       if (MODE != kNope && rot) {
-        uint32_t flo[4], fhi[4];  // pair frequencies from the LDS copy of the table
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint2 f = kfreq[rot - 1][ks * 8 + lg * 4 + e];
-          flo[e] = f.x;
-          fhi[e] = f.y;
+        for (int e = 0; e < 4; ++e) {  // pair frequencies from the LDS copy of the table
+          float sn, cs, y0, y1;
+          ksincos(r, kfreq[rot - 1][ks * 8 + lg * 4 + e], sn, cs);
+          rot_pair(bf16_lo(x[e]), bf16_hi(x[e]), cs, sn, y0, y1);
+          x[e] = pack_bf16(y0, y1);
         }
-        x = rotate_chunk(x, r, flo, fhi);
       }
       qreg[ks] = x;
     }
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
          // instruction instead of a conversion and a scaling; the truncation
          // moves the angle by under 2^-23 turn, far below the bf16 rounding of
          // the rotated key)
-        const float x = __uint_as_float(__builtin_amdgcn_alignbit(0x7fu, phase_top(r0, kf.x, kf.y), 9));
+        const float x = __uint_as_float(__builtin_amdgcn_alignbit(0x7fu, kphase(r0, kf), 9));
         sn = __builtin_amdgcn_sinf(x);
         cs = __builtin_amdgcn_cosf(x);
       }
@@ -733,12 +737,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   for (int kk = 0; kk < 4; ++kk) pop[kk] = u32x4_t{0, 0, 0, 0};
   lds_barrier();
   trace_item(2);
+  if (MODE != kNope && !ALIBI) load_kregs(pass_of(2) ? rot1 : rot0);  // the kind of the first K tile the loop stages
 #pragma clang loop unroll(disable)
   for (int t = 0; t < T; ++t) {
-    if (MODE != kNope && !ALIBI) {
-      const int srot = pass_of(t + 2) ? rot1 : rot0;
-      if (srot != kreg_rot) load_kregs(srot);
-    }
+    // the K tiles staged from here on (t + 2 onwards) are all local ones
+    if (MODE == kBifocal && !ALIBI && t + 2 == tc0) load_kregs(rot1);
     if (kVpre) read_vpre(t);
     softmax_step(t);  // P of a tile with no kept key is zero
     if (MODE == kBifocal && t + 1 < T && pass_of(t + 1) != pass_of(t)) load_q(pass_of(t + 1));

@@ -74,21 +74,6 @@ __device__ __forceinline__ int rot_index(int p, int rot, const PrefillArgs& a) {
   return p;
 }
 
-// Rotate the 4 pairs of a 16-byte bf16 chunk by id r (pairs pair0 .. pair0+3).
-__device__ __forceinline__ u32x4_t rotate_chunk(u32x4_t x, int r, const uint32_t* flo,
-                                                const uint32_t* fhi) {
-  u32x4_t y;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float s, c;
-    rope_sincos(r, flo[e], fhi[e], s, c);
-    float y0, y1;
-    rot_pair(bf16_lo(x[e]), bf16_hi(x[e]), c, s, y0, y1);
-    y[e] = pack_bf16(y0, y1);
-  }
-  return y;
-}
-
 // ---- work items ---------------------------------------------------------
 // An item is (sequence, KV head, head subgroup, row block). Without a queue
 // every workgroup runs the one item blockIdx names. With a queue the grid is

@@ -5,7 +5,9 @@
 // non-negative int32 range. The signed forms (floor semantics for negative
 // ids) are compared with 64-bit floor division over the whole int32 range's
 // edges, and the 64-bit multiply-divide (interpolated frequencies) with a
-// 128-bit product. Prints "ok <count>" or the first mismatch.
+// 128-bit product; the rotation phase from the signed split of the frequency
+// word against 64-bit wrap-around arithmetic. Prints "ok <count>" or the first
+// mismatch.
 #include <cstdint>
 #include <cstdio>
 
@@ -96,6 +98,32 @@ int main() {
         std::printf("muldiv mismatch F=%llu num=%u den=%u\n", (unsigned long long)F, num, den);
         return 1;
       }
+    }
+  }
+  // the rotation phase from the signed split of F: top 32 bits of (r * F) mod 2^64
+  // for sign-extended r, against plain 64-bit wrap-around arithmetic
+  {
+    uint64_t x = 0x9e3779b97f4a7c15ull;
+    auto next = [&]() { x ^= x << 13; x ^= x >> 7; x ^= x << 17; return x; };
+    const int32_t edge_r[] = {INT32_MIN, INT32_MIN + 1, -65537, -1, 0, 1, 2, 65536, INT32_MAX - 1, INT32_MAX};
+    const uint64_t edge_f[] = {0ull, 1ull, 0x7fffffffull, 0x80000000ull, 0xffffffffull, 0x100000000ull,
+                               0x80000000ffffffffull, 0xffffffff80000000ull, ~0ull};
+    auto check_p = [&](int32_t r, uint64_t F) {
+      const uint32_t want = static_cast<uint32_t>((static_cast<uint64_t>(static_cast<int64_t>(r)) * F) >> 32);
+      const PhaseSplit sp = phase_split(static_cast<uint32_t>(F), static_cast<uint32_t>(F >> 32));
+      ++checked;
+      if (phase_top_split(r, sp.fls, sp.fhs) != want) {
+        std::printf("phase mismatch r=%d F=%llu\n", r, (unsigned long long)F);
+        return false;
+      }
+      return true;
+    };
+    for (int32_t r : edge_r)
+      for (uint64_t F : edge_f)
+        if (!check_p(r, F)) return 1;
+    for (int i = 0; i < 2000000; ++i) {
+      const uint64_t a = next(), F = next();
+      if (!check_p(static_cast<int32_t>(a), F)) return 1;
     }
   }
   std::printf("ok %llu\n", static_cast<unsigned long long>(checked));
