@@ -409,22 +409,38 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(const DecodeArgs a
 
   float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int c = cg; c < nc; c += CG) {
-    const float* part = wsb + size_t(c) * stride;
-    const float mc = part[0], lc = part[1];
-    // partial O starts at float offset 2: read as two float2 to stay 8-byte aligned
-    const float2 x0 = *reinterpret_cast<const float2*>(part + 2 + 4 * dv);
-    const float2 x1 = *reinterpret_cast<const float2*>(part + 4 + 4 * dv);
-    const float mn = fmaxf(m, mc);
-    if (mn == -INFINITY) continue;  // nothing kept so far
-    const float wo = __builtin_amdgcn_exp2f(m - mn), wc = __builtin_amdgcn_exp2f(mc - mn);
-    l = l * wo + lc * wc;
-    acc.x = acc.x * wo + x0.x * wc;
-    acc.y = acc.y * wo + x0.y * wc;
-    acc.z = acc.z * wo + x1.x * wc;
-    acc.w = acc.w * wo + x1.y * wc;
-    m = mn;
+  // Up to kBatch of this thread's chunks per round: all their loads go out
+  // before the first use, so a round costs one memory latency (the partials
+  // were just written by other compute units and come from memory), and the
+  // merge is branch-free (a chunk past the end, or with no kept key, has
+  // weight 0).
+  constexpr int kBatch = 4;
+  for (int c0 = cg; c0 < nc; c0 += kBatch * CG) {
+    float mc[kBatch], lc[kBatch];
+    float2 x0[kBatch], x1[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = min(c0 + u * CG, nc - 1);  // (nc >= 1 inside the loop)
+      const float* part = wsb + size_t(c) * stride;
+      const float2 ml = *reinterpret_cast<const float2*>(part);  // (m, l); partials are 8-byte aligned
+      mc[u] = c0 + u * CG < nc ? ml.x : -INFINITY;
+      lc[u] = ml.y;
+      // partial O starts at float offset 2: read as two float2 to stay 8-byte aligned
+      x0[u] = *reinterpret_cast<const float2*>(part + 2 + 4 * dv);
+      x1[u] = *reinterpret_cast<const float2*>(part + 4 + 4 * dv);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float mn = fmaxf(m, mc[u]);
+      const float mr = mn == -INFINITY ? 0.f : mn;  // nothing kept so far: both weights 0
+      const float wo = __builtin_amdgcn_exp2f(m - mr), wc = __builtin_amdgcn_exp2f(mc[u] - mr);
+      l = l * wo + lc[u] * wc;
+      acc.x = acc.x * wo + x0[u].x * wc;
+      acc.y = acc.y * wo + x0[u].y * wc;
+      acc.z = acc.z * wo + x1[u].x * wc;
+      acc.w = acc.w * wo + x1[u].y * wc;
+      m = mn;
+    }
   }
   so[cg][dv] = acc;
   if (dv == 0) {
