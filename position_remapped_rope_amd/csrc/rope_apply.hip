@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(const T* __restrict__ x
                                                          int64_t n_tokens, int H, int d,
                                                          RopeFreq f) {
   constexpr int NP = VEC / 2;
+  constexpr int kHeads = 8;
   const int cpr = d / VEC;  // chunks per row
   const int64_t n_items = n_tokens * cpr;
   for (int64_t item = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; item < n_items;
@@ -89,12 +90,26 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(const T* __restrict__ x
 #pragma unroll
     for (int i = 0; i < NP; ++i) rope_sincos(p, f.lo[c * NP + i], f.hi[c * NP + i], sn[i], cs[i]);
     const int64_t base = tok * H * int64_t(d) + c * VEC;
-    for (int h = 0; h < H; ++h) {
-      float v[VEC], r[VEC];
-      VecIO<T, VEC>::load(x + base + int64_t(h) * d, v);
+    auto rotate_store = [&](int h, const float* v) {
+      float r[VEC];
 #pragma unroll
       for (int i = 0; i < NP; ++i) rot_pair(v[2 * i], v[2 * i + 1], cs[i], sn[i], r[2 * i], r[2 * i + 1]);
       VecIO<T, VEC>::store(y + base + int64_t(h) * d, r);
+    };
+    // whole groups of kHeads heads: all of a group's loads go out before the
+    // first rotation, so a thread keeps kHeads requests in flight
+    int h = 0;
+    for (; h + kHeads <= H; h += kHeads) {
+      float v[kHeads][VEC];
+#pragma unroll
+      for (int u = 0; u < kHeads; ++u) VecIO<T, VEC>::load(x + base + int64_t(h + u) * d, v[u]);
+#pragma unroll
+      for (int u = 0; u < kHeads; ++u) rotate_store(h + u, v[u]);
+    }
+    for (; h < H; ++h) {  // the rest, one head at a time
+      float v[VEC];
+      VecIO<T, VEC>::load(x + base + int64_t(h) * d, v);
+      rotate_store(h, v);
     }
   }
 }

@@ -337,6 +337,13 @@ DEC_SMALL = [
      dict(rope_base=1e6, remap_scale=4, window_left=300, remote_map="interp"), [5000, 1, 4097]),
     ("interp_s3_d64", (2, 1500, 8, 2, 64), "bifocal",
      dict(rope_base=1e4, remap_scale=3, window_left=0, remote_map="interp"), [1500, 513]),
+    # one sequence, 32/8 heads over a 20K-key cache: the short-cache policy takes
+    # 128-key chunks, so the combine merges 157 partials (all of them) or 133 (a
+    # shorter kv_len), more than one round of its per-thread batches of 4 x 32
+    ("combine_two_rounds", (1, 20000, 32, 8, 128), "bifocal", dict(rope_base=1e6, remap_scale=4, window_left=4096),
+     [20000]),
+    ("combine_partial_round", (1, 20000, 32, 8, 128), "bifocal", dict(rope_base=1e6, remap_scale=4, window_left=4096),
+     [16999]),
 ]
 
 
