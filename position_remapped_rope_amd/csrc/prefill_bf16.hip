@@ -219,14 +219,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     kt = p ? tb1 + (t - tc0) : tb0 + t;
   };
   // Are the rotation indices of a thread's two staged K rows (ids k0 and k1,
-  // RPS keys apart, k0's index r0) one id step apart? With a period the indices
-  // themselves are compared (they wrap at P). Otherwise it is enough that the
-  // ids are RPS apart without wrapping around the int32 range: for remote ids
-  // floor(p/s), s divides RPS wherever id_step >= 0.
+  // RPS keys apart, k0's index r0) one id step apart? It is enough that the ids
+  // are RPS apart without wrapping around the int32 range: for remote ids
+  // floor(p/s), s divides RPS wherever id_step >= 0; with a period P the index
+  // r0 = k0 mod P must also stay below P - RPS, so that k1 mod P = r0 + RPS.
   auto rows_affine = [&](int k0, int k1, int r0, int rot, int id_step) __attribute__((always_inline)) {
     if (id_step < 0) return false;
-    if (MODE == kRope && a.period > 0) return rot_index<MODE>(k1, rot, a) - r0 == id_step;
-    return k1 > k0 && uint32_t(k1) - uint32_t(k0) == uint32_t(RPS);
+    const bool ids = k1 > k0 && uint32_t(k1) - uint32_t(k0) == uint32_t(RPS);
+    if (MODE == kRope && a.period > 0)  // (the ALiBi kernels, short of registers, compare the indices)
+      return ALIBI ? rot_index<MODE>(k1, rot, a) - r0 == id_step : ids && r0 < a.period - RPS;
+    return ids;
   };
 
   // ---- per-thread staging coordinates --------------------------------------
@@ -738,13 +740,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   lds_barrier();
   trace_item(2);
   if (MODE != kNope && !ALIBI) load_kregs(pass_of(2) ? rot1 : rot0);  // the kind of the first K tile the loop stages
+  // the one iteration after which the query switches to the local pass (none
+  // when either pass has no tile)
+  const int tq_switch = (MODE == kBifocal && tc0 >= 1 && tc0 < T) ? tc0 - 1 : -1;
 #pragma clang loop unroll(disable)
   for (int t = 0; t < T; ++t) {
     // the K tiles staged from here on (t + 2 onwards) are all local ones
     if (MODE == kBifocal && !ALIBI && t + 2 == tc0) load_kregs(rot1);
     if (kVpre) read_vpre(t);
     softmax_step(t);  // P of a tile with no kept key is zero
-    if (MODE == kBifocal && t + 1 < T && pass_of(t + 1) != pass_of(t)) load_q(pass_of(t + 1));
+    if (MODE == kBifocal && t == tq_switch) load_q(1);
     lds_barrier();
     // one region: PV(t), QK(t+1) (the scores of tile T, if any, are never used)
     // and the LDS stores of K tile t+2 / V tile t+1 between the MFMAs. It runs
