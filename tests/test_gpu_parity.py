@@ -28,7 +28,10 @@ def _inputs(B, S, Hq, Hkv, d, dtype, seed, ids=None):
 
 # ------------------------------------------------------------------ rope_apply
 
-@pytest.mark.parametrize("dtype,d,H", [("bf16", 128, 8), ("fp32", 64, 3), ("bf16", 6, 2), ("fp32", 256, 1)])
+# (heads go in groups of 8 loads: H = 8 and 16 are whole groups, 12 a group and a
+# rest of 4, 3, 2 and 1 a rest only)
+@pytest.mark.parametrize("dtype,d,H", [("bf16", 128, 8), ("fp32", 64, 3), ("bf16", 6, 2), ("fp32", 256, 1),
+                                       ("bf16", 128, 12), ("fp32", 128, 16)])
 def test_rope_apply_matches_oracle(dtype, d, H):
     rng = np.random.default_rng(d + H)
     B, S = 2, 300
@@ -51,8 +54,9 @@ def test_rope_apply_matches_oracle(dtype, d, H):
         assert err < 2e-6 * max(1.0, float(np.max(np.abs(ref))))
 
 
-def test_rope_apply_in_place():
-    x = W.to_dtype_tensor(np.random.default_rng(5).standard_normal((1, 64, 4, 128)).astype(np.float32), "bf16").cuda()
+@pytest.mark.parametrize("H", [4, 12])
+def test_rope_apply_in_place(H):
+    x = W.to_dtype_tensor(np.random.default_rng(5).standard_normal((1, 64, H, 128)).astype(np.float32), "bf16").cuda()
     pos = torch.arange(64, dtype=torch.int32).reshape(1, 64).cuda()
     y = P.rope_apply(x, pos, 1e4)
     x2 = x.clone()
