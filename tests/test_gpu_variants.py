@@ -72,6 +72,12 @@ NEG = [
     ("bifocal_interp_ids_wrap_int32", (1, 300, 4, 2, 64, "bf16"), "bifocal",
      dict(rope_base=1e6, remap_scale=2, window_left=40, remote_map="interp"), (1 << 31) - 120),
     ("fp32_rope_ids_wrap_int32", (1, 100, 4, 2, 64, "fp32"), "rope", dict(rope_base=1e4), (1 << 31) - 50),
+    # periods at or below the 16-key step between a thread's two staged K rows:
+    # the second row's index never follows from the first's, so every tile takes
+    # the exact path for it
+    ("rope_period_below_row_step", (1, 300, 4, 2, 128, "bf16"), "rope", dict(rope_base=1e4, period=10, window_left=150),
+     -37),
+    ("rope_period_equal_row_step", (1, 300, 4, 2, 128, "bf16"), "rope", dict(rope_base=1e4, period=16), 5),
 ]
 
 
