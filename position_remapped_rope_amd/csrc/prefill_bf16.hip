@@ -617,6 +617,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
     for (; pc < 2 * NU; ++pc) piece(pc);  // whatever is left
   };
 
+  // The bifocal kernel forms P against the current reference before any row
+  // max, and takes the max only when a lane's sum of P exceeds 2^8 (P >= 0, so
+  // a smaller sum bounds every P by 2^8): 17 instructions fewer per tile of its
+  // long items, and the same references, P and results as the max-first order
+  // wherever no P lies within a bf16 rounding of 2^8. The other modes keep the
+  // max first: in their short items the first kept tile of every row would
+  // form P twice, and keeping the scores live through P spills around the
+  // item set-up.
+  constexpr bool kSumCheck = MODE == kBifocal && !ALIBI;
   // vector phase of tile t: mask, online softmax, P -> bf16, lazy O rescale
   auto softmax_step = [&](int t) __attribute__((always_inline)) {
     bool need_lo, need_hi;
@@ -658,49 +667,77 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         for (int r = 0; r < 16; ++r)
           if (nb * 32 + 8 * (r >> 2) + (r & 3) < clo) sacc[nb][r] = -INFINITY;
     }
-    // the row max of this lane's 32 scores in 16 three-input maxima
-    auto max3 = [](float x, float y, float z) __attribute__((always_inline)) { return fmaxf(fmaxf(x, y), z); };
-    float m1[10];
-#pragma unroll
-    for (int g = 0; g < 10; ++g) {
-      const int v = 3 * g;
-      m1[g] = max3(sacc[v >> 4][v & 15], sacc[(v + 1) >> 4][(v + 1) & 15], sacc[(v + 2) >> 4][(v + 2) & 15]);
-    }
-    const float m2 = max3(max3(m1[0], m1[1], m1[2]), max3(m1[3], m1[4], m1[5]), max3(m1[6], m1[7], m1[8]));
-    // sl2 > 0, so scaling after the max is the max of the scaled scores
     const float smul = ALIBI ? 1.f : sl2;  // ALiBi scores are scaled already
-    const float mx = xhalf_max(fmaxf(m2, max3(m1[9], sacc[1][14], sacc[1][15]))) * smul;
-    rotate_k(t);
+    // the row max of this lane's 32 scores in 16 three-input maxima, and across
+    // the two lanes that hold the row; smul > 0, so scaling after the max is
+    // the max of the scaled scores
+    auto row_max = [&]() __attribute__((always_inline)) {
+      auto max3 = [](float x, float y, float z) __attribute__((always_inline)) { return fmaxf(fmaxf(x, y), z); };
+      float m1[10];
+#pragma unroll
+      for (int g = 0; g < 10; ++g) {
+        const int v = 3 * g;
+        m1[g] = max3(sacc[v >> 4][v & 15], sacc[(v + 1) >> 4][(v + 1) & 15], sacc[(v + 2) >> 4][(v + 2) & 15]);
+      }
+      const float m2 = max3(max3(m1[0], m1[1], m1[2]), max3(m1[3], m1[4], m1[5]), max3(m1[6], m1[7], m1[8]));
+      return xhalf_max(fmaxf(m2, max3(m1[9], sacc[1][14], sacc[1][15]))) * smul;
+    };
     // The reference max moves only when the tile's max exceeds it by more than
     // 8 (log2 units): P <= 2^8 stays exact in bf16 and fp32, and O and l are
     // rescaled far less often. The final O / l and LSE = m + log2 l are unchanged.
-    if (__any(mx > m_run + 8.f)) {  // some row of the wave raises its reference
-      const float mnew = mx > m_run + 8.f ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-      m_run = mnew;
-      l_run *= alpha;
+    auto raise_ref = [&](float mx) __attribute__((always_inline)) {
+      if (__any(mx > m_run + 8.f)) {  // some row of the wave raises its reference
+        const float mnew = mx > m_run + 8.f ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+        m_run = mnew;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        return true;
+      }
+      return false;
+    };
+    // P of the tile against the current reference, and this lane's sum of it
+    // (from the same bf16 P the PV product uses)
+    auto exps = [&]() __attribute__((always_inline)) {
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int nb = kk >> 1, r0 = (kk & 1) * 8;
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r0 + e], smul, -m_run));
+        const u32x4_t w = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                           pack_bf16(pv[6], pv[7])};
+        pop[kk] = w;
+        rs0 = add_bf16_pair(w[0], rs0);
+        rs1 = add_bf16_pair(w[1], rs1);
+        rs0 = add_bf16_pair(w[2], rs0);
+        rs1 = add_bf16_pair(w[3], rs1);
+      }
+      return rs0 + rs1;
+    };
+    float ts;
+    if (kSumCheck) {
+      // P first, against the current reference: a lane's P values are >= 0,
+      // so a sum of at most 2^8 bounds each of them, and only a larger sum (an
+      // infinite one while a row's reference is still -FLT_MAX) needs the max
+      rotate_k(t);
+      ts = exps();
+#pragma unroll
+      for (int u = 0; u < NU; ++u)  // the rotation stays ahead of the branch, among the exps
+#pragma unroll
+        for (int e = 0; e < 4; ++e) asm volatile("" ::"v"(krot[u][e]));
+      if (__any(!(ts <= 256.f)) && raise_ref(row_max())) ts = exps();
+    } else {
+      const float mx = row_max();
+      rotate_k(t);
+      raise_ref(mx);
+      ts = exps();
     }
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int nb = kk >> 1, r0 = (kk & 1) * 8;
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r0 + e], smul, -m_run));
-      const u32x4_t w = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
-                         pack_bf16(pv[6], pv[7])};
-      pop[kk] = w;
-      // the row sum takes the same bf16 P the PV product uses
-      rs0 = add_bf16_pair(w[0], rs0);
-      rs1 = add_bf16_pair(w[1], rs1);
-      rs0 = add_bf16_pair(w[2], rs0);
-      rs1 = add_bf16_pair(w[3], rs1);
-    }
-    l_run += rs0 + rs1;
+    l_run += ts;
     return true;
   };
 
