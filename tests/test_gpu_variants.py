@@ -105,6 +105,52 @@ def test_unfused_negative_ids():
     _compare(o, lse, o_ref, lse_ref, "bf16", "unfused negative ids")
 
 
+# ------------------------------------------------------------------ scores that rise tile by tile
+
+# Log2-unit scores of the keys of each 64-key tile (plus a little jitter): a
+# tile 7.5 or 7.9 above the reference leaves it in place although the tile's P
+# sum is far above 2^8; tiles 20 and 40 higher raise it; a low tile at the end.
+RISING_LOG2 = [0.0, 7.5, 7.9, 20.0, 27.5, 40.0, 40.5, 3.0]
+
+
+def _rising_inputs(S=512, Hq=4, Hkv=2, d=128, seed=77):
+    """q and k whose scores follow RISING_LOG2 by key tile for every query row.
+    The signal sits in the last rotary pair, whose angle stays below 1e-3 rad
+    at these ids and base 1e6, so RoPE leaves the scores almost unchanged; the
+    other dims hold small noise. The oracle takes the same bf16 inputs."""
+    rng = np.random.default_rng(seed)
+    a = 16.0
+    q = rng.normal(0.0, 0.05, (1, S, Hq, d)).astype(np.float32)
+    k = rng.normal(0.0, 0.05, (1, S, Hkv, d)).astype(np.float32)
+    v = rng.normal(0.0, 1.0, (1, S, Hkv, d)).astype(np.float32)
+    q[..., d - 2] = a
+    q[..., d - 1] = 0.0
+    log2s = np.asarray(RISING_LOG2)[np.arange(S) // 64] + rng.uniform(-0.3, 0.3, S)
+    k[0, :, :, d - 2] = (log2s / np.log2(np.e) * np.sqrt(d) / a)[:, None]
+    k[..., d - 1] = 0.0
+    pos = np.arange(S, dtype=np.int32)[None, :]
+    return {"q": W.to_dtype_tensor(q, "bf16"), "k": W.to_dtype_tensor(k, "bf16"),
+            "v": W.to_dtype_tensor(v, "bf16"), "pos": torch.from_numpy(np.ascontiguousarray(pos))}
+
+
+@pytest.mark.parametrize("mode,kw", [
+    ("bifocal", dict(rope_base=1e6, remap_scale=2, window_left=64)),
+    ("bifocal", dict(rope_base=1e6, remap_scale=2, window_left=-1)),
+    ("rope", dict(rope_base=1e6)),
+    ("nope", dict()),
+], ids=["bifocal", "bifocal_remote_only", "rope", "nope"])
+def test_prefill_rising_scores(mode, kw):
+    """The reference max's rare branches (a large P sum with no raise, and a
+    raise) against the oracle, in the bifocal kernel (P before the max) and in
+    the max-first kernels."""
+    inp = _rising_inputs()
+    q, k, v, pos = (inp[n].to(DEV) for n in ("q", "k", "v", "pos"))
+    o, lse = P.prefill(q, k, v, pos if mode != "nope" else None, mode=mode, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = O.prefill_ref(*_np(inp), mode, operand_round="bf16", **kw)
+    _compare(o, lse, o_ref, lse_ref, "bf16", f"rising scores {mode} {kw}")
+
+
 # ------------------------------------------------------------------ ALiBi on a sliding window
 
 ALIBI = [
