@@ -421,6 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // ---- per-lane LDS addresses of the PV operand (transposing reads of V) ---
   // A operand of O^T += V^T P^T for d-block db and 16-key step kk: lane (lr, lg)
   // needs V[16kk + 4lg + e][32db + lr] for e = 0..3 and V[16kk + 8 + 4lg + e][..].
+  const int lane_d = lr - 4 * lg;  // i - j offset of this lane's first score register within a wave's tile
   const int j15 = lane & 15;
   const int vrow0 = 4 * lg + (j15 >> 2);
   const int vcol0 = 16 * (lr >> 4) + 4 * (j15 & 3);
@@ -636,9 +637,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
       rotate_k(t);
       return false;
     }
-    const int dbase = (i0 + lr) - (j0 + 4 * lg);  // i - j of register 0 of block 0
+    // i - j of register 0 of block 0 is (i0 - j0) + (lr - 4 lg): a wave-uniform
+    // part (scalar) and a per-lane constant, folded with the bounds below
     if (ALIBI) {  // logits in log2 units: s * scale - slope * (i - j)
-      const float b0 = -slope2 * static_cast<float>(dbase);
+      const float b0 = -slope2 * static_cast<float>(lane_d + (i0 - j0));
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -648,11 +650,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         }
     }
     // Keep dlo <= i - j <= dhi, i.e. dbase - dhi <= c <= dbase - dlo for the key
-    // offset c = j - j0 - 4 lg of a register, a constant: each bound that cuts
-    // the tile costs one compare and one select per score. (A live tile has
-    // dlo <= S and dhi >= -S, so neither difference overflows.)
+    // offset c = j - j0 - 4 lg of a register, a constant, with dbase the i - j
+    // of register 0 of block 0: each bound that cuts the tile costs one compare
+    // and one select per score. (A live tile has dlo <= S and dhi >= -S, so
+    // neither difference overflows.)
     if (need_lo) {
-      const int chi = dbase - dlo;
+      const int chi = lane_d + (i0 - j0 - dlo);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -660,7 +663,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
           if (nb * 32 + 8 * (r >> 2) + (r & 3) > chi) sacc[nb][r] = -INFINITY;
     }
     if (need_hi) {
-      const int clo = dbase - dhi;
+      const int clo = lane_d + (i0 - j0 - dhi);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
