@@ -48,6 +48,21 @@ def prefill_flops(w) -> float:
     return 4.0 * w.d * w.Hq * w.B * n_pairs(w.S, left)
 
 
+def prefill_bytes(w) -> float:
+    """Compulsory HBM bytes of one prefill launch: q, k, v (and the ids) read
+    once, o written once; no LSE (the bench does not request it)."""
+    el = 2 if w.dtype == "bf16" else 4
+    ids = 4 * w.B * w.S if w.mode != "nope" else 0
+    return float(el * w.B * w.S * w.d * (2 * w.Hq + 2 * w.Hkv) + ids)
+
+
+def roofline_time_us(flops: float, nbytes: float, peak_tflops: float):
+    """The roofline's lower bound on a launch's time (us) and the unit that sets it."""
+    t_mfma = flops / (peak_tflops * 1e12) * 1e6
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e6
+    return (t_mfma, "mfma") if t_mfma >= t_hbm else (t_hbm, "hbm")
+
+
 def kernel_source_sha(names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -214,7 +229,10 @@ def bench_prefill(name, steps, warmup, unfused=False, min_seconds=0.0, item_trac
     flops = prefill_flops(w)
     tflops = flops / (avg * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
-    r = dict(avg_ms=avg, steps_timed=steps, flops=flops, tflops=tflops, frac=tflops / peak)
+    nbytes = prefill_bytes(w)
+    t_roof, bound = roofline_time_us(flops, nbytes, peak)
+    r = dict(avg_ms=avg, steps_timed=steps, flops=flops, tflops=tflops, frac=tflops / peak, bytes=nbytes,
+             roofline_us=t_roof, roofline_bound=bound, frac_roofline=t_roof / (avg * 1e3))
     if item_trace:
         r["item_trace"] = item_trace_summary(step, launches=max(2, min(50, int(200.0 / max(avg, 1e-3)))))
     return w, inp, r
@@ -419,7 +437,11 @@ def main():
             _, _, r = bench_prefill(name, st, 3, min_seconds=0.1)
             extra[name] = {"tflops": round(r["tflops"], 2), "avg_ms": round(r["avg_ms"], 4), "flop": r["flops"],
                            "frac_peak": round(r["frac"], 4),
-                           "peak": "bf16 MFMA 2500" if name != "endprompt_fp32" else "fp32 vector 157.3"}
+                           "peak": "bf16 MFMA 2500" if name != "endprompt_fp32" else "fp32 vector 157.3",
+                           # the larger of the compute time at that peak and the
+                           # compulsory q/k/v/ids/o traffic at 8 TB/s
+                           "hbm_bytes": r["bytes"], "roofline_us": round(r["roofline_us"], 2),
+                           "roofline_bound": r["roofline_bound"], "frac_roofline": round(r["frac_roofline"], 4)}
         for name, st in (("bifocal_decode_128k_b1", 50), ("bifocal_decode_128k_b8", 10)):
             d = bench_decode(name, st, 3)
             extra[name] = {"gbs": round(d["gbs"], 1), "frac_hbm_peak": round(d["frac"], 4),
