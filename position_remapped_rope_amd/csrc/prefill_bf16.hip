@@ -536,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
   // Matrix phase of iteration t: PV(t) (16 MFMAs), then QK(t+1) (16 MFMAs),
   // with the LDS stores of this thread's rows of K tile t+2 and V tile t+1 one
   // per MFMA slot, scheduling barriers keeping that order. Operand reads run
-  // one PV step / three QK steps ahead of their MFMAs.
+  // one PV step / two QK steps ahead of their MFMAs.
   // NoPE: the V operands of the first two PV steps (keys 0-31, which this
   // wave's group staged itself) are read at the start of the vector phase,
   // which has no rotation work to hide and leaves this wave's LDS port idle
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const Prefill
         dst[db] = u32x4_t{va[0], va[1], vb[0], vb[1]};
       }
     };
-    constexpr int KA = 3;  // K steps read ahead
+    constexpr int KA = 2;  // K steps read ahead
     u32x4_t kop[KA + 1][2];
     auto read_k = [&](int ks, u32x4_t* dst) __attribute__((always_inline)) {
 #pragma unroll
