@@ -15,8 +15,9 @@ struct VecIO;
 
 template <>
 struct VecIO<uint16_t, 8> {  // 8 bf16 = 16 B
-  static __device__ __forceinline__ void load(const uint16_t* p, float* x) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
+  using Raw = uint4;
+  static __device__ __forceinline__ Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  static __device__ __forceinline__ void unpack(const Raw& w, float* x) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -36,8 +37,9 @@ struct VecIO<uint16_t, 8> {  // 8 bf16 = 16 B
 
 template <>
 struct VecIO<uint16_t, 2> {  // one pair
-  static __device__ __forceinline__ void load(const uint16_t* p, float* x) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+  using Raw = uint32_t;
+  static __device__ __forceinline__ Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  static __device__ __forceinline__ void unpack(const Raw& w, float* x) {
     x[0] = bf16_lo(w);
     x[1] = bf16_hi(w);
   }
@@ -48,9 +50,14 @@ struct VecIO<uint16_t, 2> {  // one pair
 
 template <>
 struct VecIO<float, 8> {
-  static __device__ __forceinline__ void load(const float* p, float* x) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
+  struct Raw {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ Raw load_raw(const float* p) {
+    return Raw{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+  }
+  static __device__ __forceinline__ void unpack(const Raw& w, float* x) {
+    const float4 a = w.a, b = w.b;
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
@@ -62,8 +69,9 @@ struct VecIO<float, 8> {
 
 template <>
 struct VecIO<float, 2> {
-  static __device__ __forceinline__ void load(const float* p, float* x) {
-    const float2 a = *reinterpret_cast<const float2*>(p);
+  using Raw = float2;
+  static __device__ __forceinline__ Raw load_raw(const float* p) { return *reinterpret_cast<const float2*>(p); }
+  static __device__ __forceinline__ void unpack(const Raw& a, float* x) {
     x[0] = a.x;
     x[1] = a.y;
   }
@@ -85,32 +93,55 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(const T* __restrict__ x
        item += int64_t(gridDim.x) * blockDim.x) {
     const int64_t tok = item / cpr;
     const int c = static_cast<int>(item - tok * cpr);
-    const int32_t p = pos[tok];
-    float sn[NP], cs[NP];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) rope_sincos(p, f.lo[c * NP + i], f.hi[c * NP + i], sn[i], cs[i]);
     const int64_t base = tok * H * int64_t(d) + c * VEC;
-    auto rotate_store = [&](int h, const float* v) {
-      float r[VEC];
+    // the id and the pair frequencies first, then whole groups of kHeads
+    // heads: all of a group's loads go out before the first rotation, so a
+    // thread keeps kHeads requests in flight, and the first group's loads are
+    // issued before the sin/cos, which wait only for the id and frequencies
+    // (loads complete in order)
+    const int32_t p = pos[tok];
+    uint32_t flo[NP], fhi[NP];
 #pragma unroll
-      for (int i = 0; i < NP; ++i) rot_pair(v[2 * i], v[2 * i + 1], cs[i], sn[i], r[2 * i], r[2 * i + 1]);
+    for (int i = 0; i < NP; ++i) {
+      flo[i] = f.lo[c * NP + i];
+      fhi[i] = f.hi[c * NP + i];
+    }
+    typename VecIO<T, VEC>::Raw v[kHeads];
+    auto load_group = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kHeads; ++u) v[u] = VecIO<T, VEC>::load_raw(x + base + int64_t(h + u) * d);
+    };
+    float sn[NP], cs[NP];
+    auto angles = [&](int32_t r) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) rope_sincos(r, flo[i], fhi[i], sn[i], cs[i]);
+    };
+    auto rotate_store = [&](int h, const typename VecIO<T, VEC>::Raw& w) {
+      float xv[VEC], r[VEC];
+      VecIO<T, VEC>::unpack(w, xv);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) rot_pair(xv[2 * i], xv[2 * i + 1], cs[i], sn[i], r[2 * i], r[2 * i + 1]);
       VecIO<T, VEC>::store(y + base + int64_t(h) * d, r);
     };
-    // whole groups of kHeads heads: all of a group's loads go out before the
-    // first rotation, so a thread keeps kHeads requests in flight
     int h = 0;
-    for (; h + kHeads <= H; h += kHeads) {
-      float v[kHeads][VEC];
+    if (H >= kHeads) {  // (one straight block from the loads to the sin/cos, so their wait is exact)
+      load_group(0);
+      // the id passes through an empty asm after the loads, so that the
+      // compiler cannot hoist its phase arithmetic (and the wait for it)
+      // above them
+      int32_t r = p;
+      asm volatile("" : "+v"(r));
+      angles(r);
+      for (; h + kHeads <= H; h += kHeads) {
+        if (h > 0) load_group(h);
 #pragma unroll
-      for (int u = 0; u < kHeads; ++u) VecIO<T, VEC>::load(x + base + int64_t(h + u) * d, v[u]);
-#pragma unroll
-      for (int u = 0; u < kHeads; ++u) rotate_store(h + u, v[u]);
+        for (int u = 0; u < kHeads; ++u) rotate_store(h + u, v[u]);
+      }
+    } else {
+      angles(p);
     }
-    for (; h < H; ++h) {  // the rest, one head at a time
-      float v[VEC];
-      VecIO<T, VEC>::load(x + base + int64_t(h) * d, v);
-      rotate_store(h, v);
-    }
+    for (; h < H; ++h)  // the rest, one head at a time
+      rotate_store(h, VecIO<T, VEC>::load_raw(x + base + int64_t(h) * d));
   }
 }
 
