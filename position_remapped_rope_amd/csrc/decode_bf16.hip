@@ -84,7 +84,10 @@ __device__ __forceinline__ float xgroup_sum(float x) {
   return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
 }
 
-template <int D, int MODE>
+// EARLY: the first step's K/V loads go out before the query rotation (the
+// 1-head layout; the 4-head layout keeps them after the phase tables, which
+// measured faster there)
+template <int D, int MODE, bool EARLY>
 __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const DecodeArgs a) {
   constexpr int KSTEPS = D / 32;             // 16x16x32 k-steps over the head dimension
   constexpr int DBLK = D / 16;               // 16-dim blocks of O
@@ -155,11 +158,51 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
     return a.interp ? x : static_cast<int>(fastdiv(static_cast<uint32_t>(x), sdv)) - x;
   };
   const int dq = MODE == kBifocal ? corr(pq) : 0;
+  // this wave's keys
+  const int per_wave = a.chunk / kw;
+  const int wbeg = jbeg + (wave / hpw) * per_wave;
+  const int wend = min(jend, wbeg + per_wave);
+  const uint32_t rowk_b = uint32_t(a.Hkv) * D * 2;
+  const size_t bofs = size_t(b) * a.Lmax * a.Hkv * D + size_t(kvh) * D;
+  const uint32_t span = uint32_t(jend) * rowk_b;  // loads at or past jend read 0
+  const __amdgpu_buffer_rsrc_t kres = make_rsrc(static_cast<const uint16_t*>(a.k) + bofs, span);
+  const __amdgpu_buffer_rsrc_t vres = make_rsrc(static_cast<const uint16_t*>(a.v) + bofs, span);
+
+  u32x4_t kraw[2][KSTEPS], vraw[VPL];
+  auto load_v = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int c = lane + 64 * u;  // chunk c: key c / (D/8), 16-byte column c % (D/8)
+      vraw[u] = bload16(vres, uint32_t(j0 + c / (D / 8)) * rowk_b + (c % (D / 8)) * 16);
+    }
+  };
+  auto load_k = [&](int j0, int blk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      kraw[blk][ks] = bload16(kres, uint32_t(j0 + 16 * blk + kl) * rowk_b + (8 * kg + 32 * ks) * 2);
+  };
+
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4_t w = {0, 0, 0, 0};
     if (kl < G) w = *reinterpret_cast<const u32x4_t*>(qg + size_t(kl) * D + 8 * kg + 32 * ks);
     qloc[ks] = w;
+  }
+  // EARLY: the first step's K/V loads between the query's loads and its
+  // rotation, whose VALU work (and the phase tables') then overlaps their
+  // latency. They are unconditional: a wave with no keys has wbeg >= jend, so
+  // they fall past the resources' span and read 0, and with no branch around
+  // them the wait before the rotation counts exactly the loads issued after
+  // the query's (behind a branch it waits for all of them).
+  if constexpr (EARLY) {
+    load_v(wbeg);
+    load_k(wbeg, 0);
+    load_k(wbeg, 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const u32x4_t w = qloc[ks];
     if (MODE == kBifocal) {
       u32x4_t y;
 #pragma unroll
@@ -184,10 +227,6 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   const int sdiv = static_cast<int>(sdv.div);
   const bool affine = a.interp || (16 % sdiv) == 0;
   uint32_t ph[KSTEPS][4], inc[KSTEPS][4];
-  // this wave's keys
-  const int per_wave = a.chunk / kw;
-  const int wbeg = jbeg + (wave / hpw) * per_wave;
-  const int wend = min(jend, wbeg + per_wave);
   if (MODE == kBifocal) {
     const int dk0 = corr(wbeg + kl);
     const int d16 = a.interp ? 16 : affine ? 16 / sdiv - 16 : 0;
@@ -201,26 +240,6 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
       }
   }
 
-  const uint32_t rowk_b = uint32_t(a.Hkv) * D * 2;
-  const size_t bofs = size_t(b) * a.Lmax * a.Hkv * D + size_t(kvh) * D;
-  const uint32_t span = uint32_t(jend) * rowk_b;  // loads at or past jend read 0
-  const __amdgpu_buffer_rsrc_t kres = make_rsrc(static_cast<const uint16_t*>(a.k) + bofs, span);
-  const __amdgpu_buffer_rsrc_t vres = make_rsrc(static_cast<const uint16_t*>(a.v) + bofs, span);
-
-  u32x4_t kraw[2][KSTEPS], vraw[VPL];
-  auto load_v = [&](int j0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < VPL; ++u) {
-      const int c = lane + 64 * u;  // chunk c: key c / (D/8), 16-byte column c % (D/8)
-      vraw[u] = bload16(vres, uint32_t(j0 + c / (D / 8)) * rowk_b + (c % (D / 8)) * 16);
-    }
-  };
-  auto load_k = [&](int j0, int blk) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      kraw[blk][ks] = bload16(kres, uint32_t(j0 + 16 * blk + kl) * rowk_b + (8 * kg + 32 * ks) * 2);
-  };
-
   float m_run = -INFINITY, l_run = 0.f;  // per head kl (replicated over the 4 lane groups)
   f32x4_t oacc[DBLK];
 #pragma unroll
@@ -232,7 +251,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_split_kernel(const Decode
   // Loads of the next step go out as soon as the registers they fill are free:
   // V right after this step's V is in LDS, each K block right after its scores,
   // so their latency overlaps this step's rotation and MFMA work.
-  if (wbeg < wend) {
+  if (!EARLY && wbeg < wend) {
     load_v(wbeg);
     load_k(wbeg, 0);
     load_k(wbeg, 1);
@@ -477,8 +496,12 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(const DecodeArgs a
 
 template <int D, int MODE>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, MODE>), dim3(a.n_chunks, a.Hkv / a.hpw, a.B), dim3(kDThreads), 0,
-                     stream, a);
+  if (a.hpw == 1)
+    hipLaunchKernelGGL((decode_split_kernel<D, MODE, true>), dim3(a.n_chunks, a.Hkv / a.hpw, a.B), dim3(kDThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, MODE, false>), dim3(a.n_chunks, a.Hkv / a.hpw, a.B), dim3(kDThreads),
+                       0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.B), dim3(1024), 0, stream, a);
