@@ -364,6 +364,24 @@ def test_decode_small(name, shape, mode, kw, lens):
     assert float(np.max(np.abs(lse.cpu().numpy() - lse_ref))) < LSE_TOL["bf16"]
 
 
+def test_decode_one_head_layout_waves_without_keys():
+    """The 1-head decode layout (Hkv = 2, not a multiple of 4) issues each wave's
+    first K/V loads before the query rotation whatever its key count: in the
+    last chunk of the 13333-key sequence (512-key chunks, 128 keys per wave)
+    only 21 keys remain, so three of its four waves have none and their loads
+    fall past the buffer span. Both sequences match the oracle."""
+    B, L, Hq, Hkv, d = 2, 20000, 8, 2, 128
+    kw = dict(rope_base=1e6, remap_scale=4, window_left=700)
+    w = W.Workload("t", "decode", B=B, S=L, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", mode="bifocal",
+                   rope_base=1e6, seed=517)
+    inp = W.make_decode_inputs(w)
+    inp["kv_len"] = torch.tensor([20000, 13333], dtype=torch.int32)
+    o, lse = gpu_decode(inp, mode="bifocal", **kw)
+    o_ref, lse_ref = oracle_decode(inp, "bifocal", **kw)
+    assert_close(to_np(o), o_ref, "bf16", "1-head layout, waves without keys")
+    assert float(np.max(np.abs(lse.cpu().numpy() - lse_ref))) < LSE_TOL["bf16"]
+
+
 @pytest.mark.parametrize("mode,kw", [
     ("bifocal", dict(rope_base=1e6, remap_scale=4, window_left=300)),
     ("nope", dict(window_left=100)),
